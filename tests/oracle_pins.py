@@ -1,0 +1,293 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees with: a library routine, a closed form, an invariant the pages fix, a
+hand-derived example, or brute force on tiny inputs. ``PINS`` lists them; the
+test-suite runs them on the real oracle (all must pass) and on deliberately
+broken builds of it (each must be caught by at least one pin).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+from scipy.special import expit, softmax
+
+from moe_inputs import bf16_bits_to_f32, f32_to_bf16_bits, to_float64
+from oracle import ref_numpy
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_examples.json")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand_bf16(rng, shape, std=1.0):
+    return f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+
+
+def _rand_f32(rng, shape, std=1.0):
+    return (rng.standard_normal(shape) * std).astype(np.float32)
+
+
+def _dense_gate(idx, w, E):
+    G = np.zeros((idx.shape[0], E))
+    np.put_along_axis(G, idx.astype(np.int64), w, axis=1)
+    return G
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    scale = max(np.max(np.abs(b)), 1e-300)
+    err = np.max(np.abs(a - b)) / scale if a.size else 0.0
+    assert err <= rtol, f"{what}: max|diff|/max|ref| = {err:.3e} > {rtol:.1e}"
+
+
+# --- router ------------------------------------------------------------------
+
+def pin_logits_match_library_gemv(o):
+    """Router logits x . W_g (crackai page, Top-2 Routing in Detail; notion page,
+    sparse-gating equation) equal numpy's float64 matrix product on exactly
+    widened inputs, for bf16 and fp32 storage and a non-square W_g."""
+    rng = _rng(1)
+    for dt in ("bf16", "f32"):
+        for (T, d, E) in ((37, 96, 8), (5, 64, 3)):
+            if dt == "bf16":
+                x, wg = _rand_bf16(rng, (T, d)), _rand_bf16(rng, (d, E))
+            else:
+                x, wg = _rand_f32(rng, (T, d)), _rand_f32(rng, (d, E))
+            ref = to_float64(x, dt) @ to_float64(wg, dt)
+            _close(o.logits(x, wg, dt), ref, 1e-13, f"logits {dt} {T}x{d}x{E}")
+
+
+def pin_bf16_widening_exact(o):
+    """bf16 storage is widened exactly: known bit patterns give known logits."""
+    bits = np.array([[0x3F80, 0xC020, 0x3F00, 0x4100]], dtype=np.uint16)  # 1, -2.5, 0.5, 8
+    wg = f32_to_bf16_bits(np.eye(4, dtype=np.float32))
+    l = o.logits(bits, wg, "bf16")
+    assert np.array_equal(l, np.array([[1.0, -2.5, 0.5, 8.0]])), l
+    assert np.array_equal(bf16_bits_to_f32(bits).astype(np.float64), l)
+
+
+def pin_topk_is_masked_softmax(o):
+    """G(x) = Softmax(TopK(l)) with every non-top-K logit at -inf (notion page,
+    sparse-gating equation): dense gate equals scipy's softmax of the masked
+    logits, for K = 1, 2, 3."""
+    rng = _rng(2)
+    l = rng.standard_normal((300, 8)) * 2.0
+    for K in (1, 2, 3):
+        idx, w, _ = o.topk(l, K)
+        ref_sets = ref_numpy.topk_sets(l, K)
+        assert np.array_equal(np.sort(idx, 1), np.sort(ref_sets, 1)), f"top-{K} sets"
+        G = _dense_gate(idx, w, 8)
+        G_ref = ref_numpy.masked_softmax_gate(l, K)
+        assert np.max(np.abs(G - G_ref)) <= 1e-15, f"masked softmax K={K}"
+
+
+def pin_topk_matches_softmax_then_renormalise(o):
+    """The ml-canon page's snippet (softmax over all 8, keep 2, divide by their
+    sum) gives the same sets, order and weights as the oracle."""
+    rng = _rng(3)
+    l = rng.standard_normal((400, 8)) * 1.5
+    idx, w, _ = o.topk(l, 2)
+    idx2, w2 = ref_numpy.softmax_topk_renorm_gate(l, 2)
+    assert np.array_equal(idx, idx2), "slot order / sets"
+    assert np.max(np.abs(w - w2)) <= 1e-15, np.max(np.abs(w - w2))
+
+
+def pin_two_way_closed_form(o):
+    """With two kept logits l_a >= l_b: w_a = sigma(l_a - l_b), w_b = 1 - w_a,
+    and the slot-0 expert has the larger logit (crackai page, y = w_1 E_i1 + w_2 E_i2)."""
+    rng = _rng(4)
+    l = rng.standard_normal((500, 8)) * 3.0
+    idx, w, _ = o.topk(l, 2)
+    la = np.take_along_axis(l, idx[:, :1].astype(np.int64), 1)[:, 0]
+    lb = np.take_along_axis(l, idx[:, 1:].astype(np.int64), 1)[:, 0]
+    assert np.all(la >= lb)
+    assert np.max(np.abs(w[:, 0] - expit(la - lb))) <= 2e-16
+    assert np.max(np.abs(w.sum(1) - 1.0)) <= 4.5e-16
+
+
+def pin_weights_sum_to_one(o):
+    """The kept weights of every token sum to 1 (softmax over the kept logits)."""
+    rng = _rng(5)
+    l = rng.standard_normal((200, 8)) * 4.0
+    for K in (1, 2, 4, 8):
+        _, w, _ = o.topk(l, K)
+        assert np.max(np.abs(w.sum(1) - 1.0)) <= 1e-15, K
+
+
+def pin_full_softmax_when_K_equals_E(o):
+    """K = E keeps every expert: the gate is the plain softmax of the logits."""
+    rng = _rng(6)
+    l = rng.standard_normal((100, 8))
+    idx, w, margin = o.topk(l, 8)
+    assert np.max(np.abs(_dense_gate(idx, w, 8) - softmax(l, axis=1))) <= 1e-15
+    assert np.all(np.isinf(margin))
+
+
+def pin_tie_break_and_margin(o):
+    """Exact ties go to the lower expert index; margin = last kept minus the
+    largest dropped logit (numpy sort)."""
+    l = np.array([[0.5, 2.0, 2.0, 1.0, -1.0, 2.0, 0.0, 0.0],
+                  [1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0],
+                  [3.0, -1.0, 2.0, 2.0, 0.0, 0.0, 0.0, 0.0]])
+    idx, w, margin = o.topk(l, 2)
+    assert idx.tolist() == [[1, 2], [0, 1], [0, 2]], idx.tolist()
+    assert margin.tolist() == [0.0, 0.0, 0.0], margin.tolist()
+    rng = _rng(7)
+    l = rng.standard_normal((300, 8))
+    for K in (1, 2, 3):
+        _, _, margin = o.topk(l, K)
+        s = -np.sort(-l, axis=1)
+        assert np.array_equal(margin, s[:, K - 1] - s[:, K]), K
+
+
+def pin_shift_invariance(o):
+    """Adding one constant to every logit (through a constant input feature and
+    a constant W_g row) changes neither the sets nor the weights."""
+    rng = _rng(8)
+    T, d = 64, 32
+    x = _rand_f32(rng, (T, d))
+    x[:, 0] = 1.0
+    wg = _rand_f32(rng, (d, 8), 0.3)
+    wg[0, :] = 0.0
+    idx0, w0, _ = o.topk(o.logits(x, wg, "f32"), 2)
+    wg[0, :] = 0.75
+    idx1, w1, _ = o.topk(o.logits(x, wg, "f32"), 2)
+    assert np.array_equal(idx0, idx1)
+    assert np.max(np.abs(w0 - w1)) <= 1e-14
+
+
+def pin_set_weights(o):
+    """Weights of a given set are the masked softmax over that set."""
+    rng = _rng(9)
+    l = rng.standard_normal((50, 8))
+    idx, w, _ = o.topk(l, 2)
+    assert np.max(np.abs(o.set_weights(l, idx) - w)) <= 1e-16
+    other = np.stack([idx[:, 1], (idx[:, 1] + 1) % 8], 1).astype(np.int32)
+    other[other[:, 1] == idx[:, 0], 1] = (other[other[:, 1] == idx[:, 0], 1] + 1) % 8
+    ws = o.set_weights(l, other)
+    la = np.take_along_axis(l, other[:, :1].astype(np.int64), 1)[:, 0]
+    lb = np.take_along_axis(l, other[:, 1:].astype(np.int64), 1)[:, 0]
+    assert np.max(np.abs(ws[:, 0] - expit(la - lb))) <= 2e-16
+
+
+# --- permute -----------------------------------------------------------------
+
+def pin_permute_is_stable_sort(o):
+    """Gathering tokens by expert (ml-canon page, Questions worth asking) as a
+    stable sort of the T*K slots by expert id equals numpy's stable argsort;
+    offsets are the cumulative counts; slot_pos inverts perm."""
+    rng = _rng(10)
+    for (T, E, K) in ((1, 8, 2), (97, 8, 2), (50, 3, 1), (64, 8, 8)):
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+        off, perm, slot = o.permute(idx, E)
+        flat = idx.reshape(-1)
+        order = np.argsort(flat, kind="stable")
+        assert np.array_equal(perm, order // K), (T, E, K)
+        inv = np.empty_like(order)
+        inv[order] = np.arange(order.size)
+        assert np.array_equal(slot.reshape(-1), inv)
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+
+
+# --- expert FFN and the whole layer ---------------------------------------------
+
+def _tiny_layer(rng, T, d, h, E, dt, std=0.5):
+    mk = _rand_bf16 if dt == "bf16" else _rand_f32
+    return {"x": mk(rng, (T, d)), "w_g": mk(rng, (d, E), std),
+            "w1": mk(rng, (E, h, d), std), "w3": mk(rng, (E, h, d), std),
+            "w2": mk(rng, (E, d, h), std)}
+
+
+def _f64(inp, dt):
+    return {k: to_float64(v, dt) for k, v in inp.items()}
+
+
+def pin_gate_up_and_down_match_matmul(o):
+    """The expert's two halves: act = silu(W1 x) * (W3 x), out = W2 act, against
+    numpy matrix products with silu(z) = z * expit(z); non-square (d != h)."""
+    rng = _rng(11)
+    for dt in ("bf16", "f32"):
+        n, d, h = 21, 48, 80
+        mk = _rand_bf16 if dt == "bf16" else _rand_f32
+        x, w1, w3, w2 = mk(rng, (n, d)), mk(rng, (h, d), .3), mk(rng, (h, d), .3), mk(rng, (d, h), .3)
+        xf, w1f, w3f, w2f = (to_float64(a, dt) for a in (x, w1, w3, w2))
+        g, u = xf @ w1f.T, xf @ w3f.T
+        act_ref = g * expit(g) * u
+        act = o.gate_up(x, w1, w3, dt)
+        _close(act, act_ref, 1e-13, f"gate_up {dt}")
+        act32 = act_ref.astype(np.float32)
+        act_st = f32_to_bf16_bits(act32) if dt == "bf16" else act32
+        _close(o.down(act_st, dt, w2, dt), to_float64(act_st, dt) @ w2f.T, 1e-13, f"down {dt}")
+
+
+def pin_E1_K1_is_dense_swiglu(o):
+    """E = 1, K = 1: the gate weight is exactly 1 and the layer is one dense
+    SwiGLU FFN (numpy matrix products); d != h catches transposed operands."""
+    rng = _rng(12)
+    T, d, h = 9, 24, 40
+    inp = _tiny_layer(rng, T, d, h, 1, "f32")
+    res = o.forward(inp, 1, "f32")
+    assert np.all(res["w"] == 1.0) and np.all(res["idx"] == 0)
+    f = _f64(inp, "f32")
+    _close(res["y"], ref_numpy.dense_swiglu(f["x"], f["w1"][0], f["w3"][0], f["w2"][0]), 1e-12,
+           "E=1,K=1 vs dense SwiGLU")
+
+
+def pin_identical_experts(o):
+    """All experts identical: y equals that one expert's output for any router
+    (the weights sum to 1)."""
+    rng = _rng(13)
+    T, d, h, E = 20, 32, 48, 8
+    inp = _tiny_layer(rng, T, d, h, E, "bf16")
+    for k in ("w1", "w3", "w2"):
+        inp[k] = np.ascontiguousarray(np.broadcast_to(inp[k][:1], inp[k].shape))
+    res = o.forward(inp, 2, "bf16")
+    f = _f64(inp, "bf16")
+    _close(res["y"], ref_numpy.dense_swiglu(f["x"], f["w1"][0], f["w3"][0], f["w2"][0]), 1e-13,
+           "identical experts")
+
+
+def pin_brute_force_dense_masked_sum(o):
+    """Tiny inputs: the oracle's sparse evaluation equals the brute-force dense
+    sum over all n experts with the masked gate (notion page, output equation
+    y = sum_i G(x)_i E_i(x))."""
+    rng = _rng(14)
+    for (T, d, h, E, K, dt) in ((16, 32, 64, 8, 2, "f32"), (13, 16, 32, 5, 2, "bf16"),
+                                (8, 32, 16, 4, 1, "f32")):
+        inp = _tiny_layer(rng, T, d, h, E, dt)
+        res = o.forward(inp, K, dt)
+        f = _f64(inp, dt)
+        _close(res["y"], ref_numpy.dense_moe(f["x"], f["w_g"], f["w1"], f["w3"], f["w2"], K),
+               1e-13, f"brute force {T},{d},{h},{E},{K},{dt}")
+
+
+def pin_hand_examples(o):
+    """Hand-derived closed-form examples (tests/golden/hand_examples.json)."""
+    with open(GOLDEN) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        inp = {k: np.array(c[k], dtype=np.float32) for k in ("x", "w_g", "w1", "w3", "w2")}
+        res = o.forward(inp, c["K"], "f32")
+        assert res["idx"].tolist() == c["idx"], (c["name"], res["idx"])
+        assert np.max(np.abs(res["w"] - np.array(c["w"]))) <= 2e-16, c["name"]
+        assert np.max(np.abs(res["y"] - np.array(c["y"]))) <= 1e-15, (c["name"], res["y"])
+
+
+def pin_token_subset_consistent(o):
+    """Evaluating a subset of tokens gives the same rows as evaluating all (the
+    layer is per token: crackai page, routing is independent per token)."""
+    rng = _rng(15)
+    inp = _tiny_layer(rng, 40, 32, 48, 8, "bf16")
+    full = o.forward(inp, 2, "bf16")
+    sub = [39, 3, 17, 3]
+    part = o.forward(inp, 2, "bf16", tokens=sub)
+    assert np.array_equal(part["y"], full["y"][sub])
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
