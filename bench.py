@@ -1,0 +1,274 @@
+"""Benchmark of the Mixtral sparse-MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one pass of the whole layer (route -> permute -> gate-up -> down ->
+combine) over one batch of the workload's synthetic inputs, already resident in
+HBM. The default workload is the Mixtral-8x7B decode batch (T = 32 tokens,
+d = 4096, h = 14336, E = 8, K = 2, bf16), whose expert weights (2.82 GB) must be
+streamed from HBM every step; other workloads: prefill_8x7b, skew_8x7b,
+prefill_8x22b, tiny_f32.
+
+Printed: ONE JSON line with tokens/s, the dominant kernel's roofline fraction
+(HIP events around that kernel inside the timed region) and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (decode)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+MFMA_F32_PEAK_TFLOPS = 157.3    # fp32 vector/matrix peak (fp32 problems)
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_wg_amd", "csrc")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_8x7b")
+    ap.add_argument("--weight-copies", type=int, default=2,
+                    help="rotate this many copies of the expert weights so that no step "
+                         "finds them in the 256 MB last-level cache")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate budget of the CPU-oracle baseline leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", default="auto", choices=["auto", "stream", "tiled"])
+    return ap.parse_args()
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def kernel_files(path: str):
+    return ["gemm_stream.hip"] if path == "stream" else ["gemm_tiled.hip"]
+
+
+def load_traffic(workload: str, kernel: str, sha: str):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    f = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this layer has no "
+              "multi-GPU path", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import sparse_mixture_experts_wg_amd as moe
+    from tests import parity
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    cfg = mi.CONFIGS[args.workload]
+    T, d, h, E, K, S = cfg.T, cfg.d, cfg.h, cfg.E, cfg.K, cfg.S
+    print(f"# workload {cfg.name}: T={T} d={d} h={h} E={E} K={K} {cfg.dtype}; generating",
+          file=sys.stderr, flush=True)
+    inp = mi.make_inputs(cfg, seed=0)
+    dev = parity.upload_inputs({k: inp[k] for k in ("x", "w_g")}, cfg.dtype)
+    copies = max(1, args.weight_copies)
+    wsets = []
+    for c in range(copies):
+        wsets.append({k: parity.device_array(inp[k], cfg.dtype) for k in ("w1", "w3", "w2")})
+    p = moe.problem(T, d, h, E, K, cfg.dtype, "f32", args.path)
+    path = "stream" if moe.resolve_path(p) == moe.PATH_STREAM else "tiled"
+    if cfg.dtype == "f32":
+        path = "f32"
+    f32 = torch.float32
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else f32
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=f32, device="cuda")
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device="cuda")
+    perm = torch.empty((S,), dtype=torch.int32, device="cuda")
+    slot = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    x_perm = torch.empty((S, d), dtype=dt, device="cuda")
+    act = torch.empty((S, h), dtype=dt, device="cuda")
+    o_perm = torch.empty((S, d), dtype=f32, device="cuda")
+    y = torch.empty((T, d), dtype=f32, device="cuda")
+
+    def step(i, ev=None):
+        ws = wsets[i % copies]
+        if ev is not None:
+            ev[0].record()
+        moe.route(p, dev["x"], dev["w_g"], idx, w)
+        moe.permute(p, dev["x"], idx, offsets, perm, slot, x_perm)
+        if ev is not None:
+            ev[1].record()
+        moe.expert_gate_up(p, x_perm, offsets, ws["w1"], ws["w3"], act)
+        if ev is not None:
+            ev[2].record()
+        moe.expert_down(p, act, offsets, ws["w2"], o_perm)
+        if ev is not None:
+            ev[3].record()
+        moe.combine(p, o_perm, slot, w, y)
+        if ev is not None:
+            ev[4].record()
+
+    print(f"# path {path}; {args.warmup} warm-up steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    counts = np.diff(parity.host_array(offsets).astype(np.int64))
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    stage = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(4)] for ev in events])
+    stage_ms = stage.mean(axis=0)
+    gpu_ms_step = float(np.mean([ev[0].elapsed_time(ev[4]) for ev in events]))
+    tokens_per_s = T / (ms_step / 1e3)
+
+    # one-call API on the same inputs, for comparison (not part of the timed region)
+    ws_fwd = torch.empty((moe.forward_workspace_bytes(p),), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        moe.forward(p, dev["x"], dev["w_g"], wsets[0]["w1"], wsets[0]["w3"], wsets[0]["w2"], y,
+                    ws=ws_fwd)
+    torch.cuda.synchronize()
+    n_fwd = max(5, min(args.steps, 50))
+    t1 = time.perf_counter()
+    for i in range(n_fwd):
+        ws_ = wsets[i % copies]
+        moe.forward(p, dev["x"], dev["w_g"], ws_["w1"], ws_["w3"], ws_["w2"], y, ws=ws_fwd)
+    torch.cuda.synchronize()
+    ms_forward = (time.perf_counter() - t1) * 1e3 / n_fwd
+
+    # ---- roofline of the dominant kernel (gate-up) --------------------------------
+    es = 2 if cfg.dtype == "bf16" else 4
+    hit = int(np.sum(counts > 0))
+    gu_ms = float(stage_ms[1])
+    gu_bytes = hit * 2 * h * d * es + S * d * es + S * h * es
+    gu_flop = 2.0 * S * d * 2 * h
+    layer_bytes = hit * 3 * h * d * es + d * E * es + T * d * es + T * d * 4
+    layer_flop = 2.0 * S * 3 * d * h + 2.0 * T * d * E
+    kernel = {"stream": "stream_gate_up", "tiled": "tiled_gate_up", "f32": "f32_gate_up"}[path]
+    sha = source_hash(kernel_files(path)) if path != "f32" else None
+    traffic_rec = load_traffic(cfg.name, kernel, sha) if sha else None
+    traffic = None
+    if traffic_rec:
+        traffic = {"fetch_bytes": traffic_rec["fetch_bytes_per_launch"],
+                   "write_bytes": traffic_rec["write_bytes_per_launch"],
+                   "source": os.path.relpath(traffic_rec["_file"], ROOT)
+                   if "_file" in traffic_rec else f"profiles/traffic_{kernel}_{cfg.name}.json"}
+    if path == "stream":
+        achieved = gu_bytes / (gu_ms / 1e3) / 1e9
+        roof = {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": gu_bytes, "avg_launch_ms": round(gu_ms, 5),
+                "traffic": traffic}
+        layer = {"hbm_frac": round(layer_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "algorithmic_bytes": layer_bytes}
+    else:
+        peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        achieved = gu_flop / (gu_ms / 1e3) / 1e12
+        roof = {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "algorithmic_flop": gu_flop,
+                "avg_launch_ms": round(gu_ms, 5), "traffic": traffic}
+        layer = {"mfma_frac": round(layer_flop / (ms_step / 1e3) / 1e12 / peak, 4),
+                 "algorithmic_flop": layer_flop}
+
+    # ---- CPU oracle baseline on a bounded sample, plus a parity spot check ---------
+    cpu = None
+    spot = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        o = oracle.load()
+        per_tok = 2.0 * K * 3 * d * h
+        n = int(min(T, max(8, round(args.cpu_seconds * 2.0e9 * o.threads / per_tok))))
+        toks = np.arange(n)
+        print(f"# CPU oracle on {n} tokens x {o.threads} threads", file=sys.stderr, flush=True)
+        c0 = time.perf_counter()
+        passes = 0
+        while True:
+            xs = np.ascontiguousarray(inp["x"][:n])
+            l, idx_r, w_r, margin = o.route(xs, inp["w_g"], K, cfg.dtype)
+            y_ref = o.forward_tokens(toks, xs, inp["w1"], inp["w3"], inp["w2"], idx_r, w_r,
+                                     cfg.dtype)
+            passes += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds * 0.5 or passes >= 50:
+                break
+        cpu_s = (time.perf_counter() - c0) / passes
+        cpu = {"value": round(n / cpu_s, 3), "unit": "tokens/s", "cores": o.threads,
+               "kind": "oracle",
+               "sample": f"first {n} of {T} tokens of {cfg.name} (route + all K experts + "
+                         f"combine, float64), {passes} pass(es), {cpu_s:.2f} s per pass"}
+        # parity of the timed run's output on the same tokens (rule R applied)
+        ih = parity.host_array(idx)[:n]
+        wh = parity.host_array(w)[:n]
+        idx_eval, diff = parity.check_routing(ih, wh, l, idx_r, margin, K, o)
+        if len(diff):
+            y_ref = o.forward_tokens(toks, xs, inp["w1"], inp["w3"], inp["w2"], idx_eval,
+                                     o.set_weights(l, idx_eval), cfg.dtype)
+        spot_rel = parity.check_output(parity.host_array(y)[:n], y_ref, cfg.dtype, "bench")
+        spot = {"tokens": n, "max_err_over_rms": float(f"{spot_rel:.4e}"),
+                "tolerance": parity.Y_TOL[cfg.dtype]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded generator; random-init weights of the layer's shape)",
+        "config": {"workload": cfg.name, "T": T, "d": d, "h": h, "E": E, "K": K,
+                   "path": path, "weight_copies": copies},
+        "roofline": roof,
+        "layer": layer,
+        "cpu_baseline": cpu,
+        "stages_ms": {"route+permute": round(float(stage_ms[0]), 5),
+                      "gate_up": round(float(stage_ms[1]), 5),
+                      "down": round(float(stage_ms[2]), 5),
+                      "combine": round(float(stage_ms[3]), 5)},
+        "gpu_ms_per_step_events": round(gpu_ms_step, 5),
+        "ms_per_step_one_call_api": round(ms_forward, 5),
+        "rows_per_expert": counts.tolist(),
+        "parity_spot_check": spot,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

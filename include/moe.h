@@ -1,0 +1,184 @@
+/*
+ * moe.h -- C ABI of an MI355X (gfx950) implementation of the Mixtral sparse
+ * mixture-of-experts feed-forward layer.
+ *
+ * The layer (Mixtral of Experts pages: crackai "Top-2 Routing in Detail";
+ * notion "Architectural details", sparse-gating and output equations):
+ *   l      = x . W_g                         router logits, [T, E]
+ *   G(x)   = Softmax(TopK(l))                every non-top-K logit -> -inf
+ *   y_t    = sum_k w_{t,k} * SwiGLU_{i_{t,k}}(x_t)
+ *   SwiGLU_e(x) = W2_e (silu(W1_e x) * (W3_e x)),  silu(z) = z / (1 + e^-z)
+ * split into the steps a GPU runs: route, permute (gather each expert's tokens
+ * into one contiguous segment), the two expert projections, and a weighted
+ * combine back to token order.
+ *
+ * Conventions for every entry point
+ *  - Every data pointer is a DEVICE pointer owned by the caller and must be
+ *    16-byte aligned. The library never allocates, frees or synchronises; all
+ *    work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    runs asynchronously. Inputs must stay valid until the work completes.
+ *  - Arrays are dense and row-major. dtype applies to x, W_g, W1, W3, W2 and the
+ *    hidden activations; router outputs, o_perm and the softmax are float32.
+ *    bf16 is stored as its 16 upper float32 bits (round-to-nearest-even).
+ *  - Inputs must be finite. Output for non-finite input is unspecified.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is enqueued and a moe_status other than MOE_OK is returned,
+ *    with a message from moe_last_error() (per thread). A device fault surfaces
+ *    at the caller's next synchronisation.
+ *  - Supported problems: 1 <= E <= 8, K in {1, 2}, K <= E, T >= 1,
+ *    T*K < 2^31, d and h positive multiples of 128.
+ *  - Results are deterministic: no atomics take part in any value, and every
+ *    sum has a fixed order.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  MOE_ERR_SHAPE = 2,       /* T, d, h, E or K < 1, or K > E                      */
+  MOE_ERR_UNSUPPORTED = 3, /* outside the supported problems listed above        */
+  MOE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                   */
+  MOE_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returns      */
+  MOE_ERR_HIP = 6          /* the HIP runtime reported an error while enqueuing  */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Expert-projection variant. STREAM: weight streaming for small batches
+ * (every expert receives at most 64 rows, guaranteed when T <= 64); TILED:
+ * LDS-tiled matrix-core GEMM for large batches. AUTO picks STREAM when
+ * T <= 64, else TILED. float32 problems always use one plain tiled kernel. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 } moe_path;
+
+typedef struct {
+  int64_t T;         /* tokens                                   */
+  int64_t d;         /* model dimension                          */
+  int64_t h;         /* expert hidden dimension (14336 in 8x7B)  */
+  int32_t E;         /* experts (8)                              */
+  int32_t K;         /* experts per token (2)                    */
+  int32_t dtype;     /* moe_dtype of x, W_g, W1, W3, W2, act     */
+  int32_t out_dtype; /* moe_dtype of y                           */
+  int32_t path;      /* moe_path                                 */
+  int32_t reserved;  /* must be 0                                */
+} moe_problem;
+
+/* Human-readable name of a status code. */
+const char *moe_status_string(int status);
+
+/* Detail of the last error returned on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Which expert-projection variant `p` runs on (MOE_PATH_STREAM or
+ * MOE_PATH_TILED), or a negative moe_status if `p` is invalid. Host only. */
+int moe_resolve_path(const moe_problem *p);
+
+/*
+ * Router: logits l = x . W_g accumulated in float32 (never rounded to bf16),
+ * the top-K experts by (logit descending, lower index first on an exact tie),
+ * and their gate weights, the softmax of the kept logits (crackai page,
+ * "Top-2 Routing in Detail"; notion page, sparse-gating equation). For K = 2:
+ * w_0 = 1 / (1 + exp(l_1 - l_0)), w_1 = exp(l_1 - l_0) * w_0.
+ *   x        [T, d]  dtype
+ *   w_g      [d, E]  dtype
+ *   topk_idx [T, K]  int32 out; slot 0 holds the larger logit
+ *   topk_w   [T, K]  float32 out
+ *   logits   [T, E]  float32 out, or NULL
+ */
+moe_status moe_route(const moe_problem *p, const void *x, const void *w_g,
+                     int32_t *topk_idx, float *topk_w, float *logits, void *stream);
+
+/*
+ * Permute: stable counting sort of the S = T*K token-slots by expert, then a
+ * row gather, so that each expert's tokens form one contiguous segment (the
+ * gather/scatter of tokens spread unevenly over experts, ml-canon page,
+ * "Questions worth asking"). Within one expert rows follow ascending slot
+ * index s = t*K + k. Expert ids outside [0, E) are dropped: their slot_pos is
+ * -1, they take no row, and offsets[E] counts only kept slots.
+ *   x          [T, d]   dtype
+ *   topk_idx   [T, K]   int32
+ *   offsets    [E + 1]  int32 out: segment e is rows offsets[e] .. offsets[e+1]-1
+ *   perm_token [S]      int32 out: token of each sorted row (rows >= offsets[E] untouched)
+ *   slot_pos   [T, K]   int32 out: sorted row of slot (t, k)
+ *   x_perm     [S, d]   dtype out: x_perm[r] = x[perm_token[r]]
+ */
+moe_status moe_permute(const moe_problem *p, const void *x, const int32_t *topk_idx,
+                       int32_t *offsets, int32_t *perm_token, int32_t *slot_pos,
+                       void *x_perm, void *stream);
+
+/*
+ * Expert gate-up projection with the SwiGLU epilogue, for every expert's
+ * segment of rows: act[r] = silu(W1_e x_r) * (W3_e x_r), accumulated in float32
+ * and rounded once to dtype (notion page, "Implementation": SwiGLU experts).
+ *   x_perm  [S, d]     dtype (rows offsets[0] .. offsets[E]-1 are read)
+ *   offsets [E + 1]    int32, non-decreasing, offsets[0] = 0, offsets[E] <= S
+ *   w1, w3  [E, h, d]  dtype
+ *   act     [S, h]     dtype out (rows >= offsets[E] untouched)
+ * The STREAM path requires offsets[e+1] - offsets[e] <= 64 for every e.
+ */
+moe_status moe_expert_gate_up(const moe_problem *p, const void *x_perm, const int32_t *offsets,
+                              const void *w1, const void *w3, void *act, void *stream);
+
+/*
+ * Expert down projection: o_perm[r] = W2_e act[r] for every expert's segment,
+ * accumulated and stored in float32.
+ *   act     [S, h]     dtype
+ *   offsets [E + 1]    int32 (as above)
+ *   w2      [E, d, h]  dtype
+ *   o_perm  [S, d]     float32 out (rows >= offsets[E] untouched)
+ */
+moe_status moe_expert_down(const moe_problem *p, const void *act, const int32_t *offsets,
+                           const void *w2, float *o_perm, void *stream);
+
+/* Bytes of workspace moe_expert_swiglu needs (0 if `p` is invalid). */
+size_t moe_expert_workspace_bytes(const moe_problem *p);
+
+/*
+ * Both expert projections: o_perm[r] = SwiGLU_e(x_perm[r]) for every segment,
+ * with the hidden activations in `ws` (at least moe_expert_workspace_bytes).
+ */
+moe_status moe_expert_swiglu(const moe_problem *p, const void *x_perm, const int32_t *offsets,
+                             const void *w1, const void *w3, const void *w2, float *o_perm,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Combine: y[t] = sum_{k=0}^{K-1} topk_w[t, k] * o_perm[slot_pos[t, k]], in
+ * float32 in k order, rounded once to out_dtype (crackai page,
+ * y = w_1 Expert_i1(x) + w_2 Expert_i2(x); notion page, output equation).
+ * Slots with slot_pos outside [0, T*K) (-1 marks a dropped slot) contribute
+ * nothing.
+ *   o_perm   [S, d]  float32
+ *   slot_pos [T, K]  int32
+ *   topk_w   [T, K]  float32
+ *   y        [T, d]  out_dtype out
+ */
+moe_status moe_combine(const moe_problem *p, const float *o_perm, const int32_t *slot_pos,
+                       const float *topk_w, void *y, void *stream);
+
+/* Bytes of workspace moe_forward needs (0 if `p` is invalid). */
+size_t moe_forward_workspace_bytes(const moe_problem *p);
+
+/*
+ * The whole layer: route -> permute -> gate-up -> down -> combine on `stream`.
+ *   x [T, d], w_g [d, E], w1/w3 [E, h, d], w2 [E, d, h] in dtype
+ *   y [T, d] out_dtype out
+ *   topk_idx [T, K] int32 and topk_w [T, K] float32: optional outputs (NULL to
+ *   keep them in the workspace)
+ *   ws: at least moe_forward_workspace_bytes(p) bytes, 256-byte aligned
+ */
+moe_status moe_forward(const moe_problem *p, const void *x, const void *w_g, const void *w1,
+                       const void *w3, const void *w2, void *y, int32_t *topk_idx,
+                       float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

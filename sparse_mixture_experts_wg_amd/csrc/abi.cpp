@@ -1,0 +1,354 @@
+// abi.cpp -- the C ABI declared in include/moe.h: host-side validation, the
+// workspace layout and the launch sequence. No allocation, no synchronisation.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
+constexpr int kStreamMaxT = 64;
+
+size_t esize(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+moe_status check_problem(const moe_problem *p) {
+  if (!p) return fail(MOE_ERR_NULL, "problem descriptor is NULL");
+  if (p->T < 1 || p->d < 1 || p->h < 1 || p->E < 1 || p->K < 1)
+    return fail(MOE_ERR_SHAPE, "T=%lld d=%lld h=%lld E=%d K=%d: every size must be >= 1",
+                (long long)p->T, (long long)p->d, (long long)p->h, p->E, p->K);
+  if (p->K > p->E) return fail(MOE_ERR_SHAPE, "K=%d exceeds E=%d", p->K, p->E);
+  if (p->E > 8) return fail(MOE_ERR_UNSUPPORTED, "E=%d: at most 8 experts", p->E);
+  if (p->K > 2) return fail(MOE_ERR_UNSUPPORTED, "K=%d: K must be 1 or 2", p->K);
+  if (p->d % 128 || p->h % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "d=%lld h=%lld: both must be multiples of 128",
+                (long long)p->d, (long long)p->h);
+  if (p->d > kMaxDim || p->h > kMaxDim)
+    return fail(MOE_ERR_UNSUPPORTED, "d=%lld h=%lld: at most 2^20", (long long)p->d,
+                (long long)p->h);
+  if (p->T > kMaxIndex / p->K || p->T > kMaxIndex / ((p->d + 1023) / 1024))
+    return fail(MOE_ERR_UNSUPPORTED, "T=%lld too large for 32-bit slot indices", (long long)p->T);
+  if ((p->dtype != MOE_F32 && p->dtype != MOE_BF16) ||
+      (p->out_dtype != MOE_F32 && p->out_dtype != MOE_BF16))
+    return fail(MOE_ERR_UNSUPPORTED, "dtype=%d out_dtype=%d: use MOE_F32 or MOE_BF16", p->dtype,
+                p->out_dtype);
+  if (p->path < MOE_PATH_AUTO || p->path > MOE_PATH_TILED)
+    return fail(MOE_ERR_UNSUPPORTED, "path=%d unknown", p->path);
+  if (p->dtype == MOE_F32 && p->path == MOE_PATH_STREAM)
+    return fail(MOE_ERR_UNSUPPORTED, "the STREAM path is bf16 only");
+  if (p->reserved != 0) return fail(MOE_ERR_UNSUPPORTED, "reserved field must be 0");
+  // tiled grid: column blocks x (token blocks + E) must fit a 1-D grid
+  const int64_t S = p->T * p->K;
+  const int64_t tiles = (p->h / 128) * ((S + 255) / 256 + p->E);
+  if (tiles > kMaxIndex / 2) return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch");
+  return MOE_OK;
+}
+
+int resolve(const moe_problem *p) {
+  if (p->dtype == MOE_F32) return MOE_PATH_TILED;
+  if (p->path != MOE_PATH_AUTO) return p->path;
+  return p->T <= kStreamMaxT ? MOE_PATH_STREAM : MOE_PATH_TILED;
+}
+
+moe_status check_ptr(const void *ptr, const char *name, bool required = true) {
+  if (!ptr) return required ? fail(MOE_ERR_NULL, "%s is NULL", name) : MOE_OK;
+  if (reinterpret_cast<uintptr_t>(ptr) % 16)
+    return fail(MOE_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+#define CHECK(expr)                   \
+  do {                                \
+    moe_status st_ = (expr);          \
+    if (st_ != MOE_OK) return st_;    \
+  } while (0)
+
+moe_status hip_result(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+struct ForwardLayout {
+  size_t idx, w, offsets, perm, slot, x_perm, act, o_perm, total;
+};
+
+ForwardLayout forward_layout(const moe_problem *p) {
+  const size_t S = size_t(p->T) * p->K;
+  ForwardLayout L{};
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at += align256(bytes);
+    return here;
+  };
+  L.idx = take(S * 4);
+  L.w = take(S * 4);
+  L.offsets = take(size_t(p->E + 1) * 4);
+  L.perm = take(S * 4);
+  L.slot = take(S * 4);
+  L.x_perm = take(S * p->d * esize(p->dtype));
+  L.act = take(S * p->h * esize(p->dtype));
+  L.o_perm = take(S * p->d * 4);
+  L.total = at;
+  return L;
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+// ---- the steps, after validation ----------------------------------------------
+
+moe_status do_route(const moe_problem *p, const void *x, const void *w_g, int32_t *idx, float *w,
+                    float *logits, hipStream_t s) {
+  return hip_result(moe::launch_route(p->dtype == MOE_BF16, x, w_g, p->T, int(p->d), p->E, p->K,
+                                      idx, w, logits, s),
+                    "route launch");
+}
+
+moe_status do_permute(const moe_problem *p, const void *x, const int32_t *idx, int32_t *offsets,
+                      int32_t *perm, int32_t *slot, void *x_perm, hipStream_t s) {
+  const int64_t S = p->T * p->K;
+  CHECK(hip_result(moe::launch_permute_index(idx, S, p->K, p->E, offsets, perm, slot, s),
+                   "permute launch"));
+  return hip_result(moe::launch_gather_rows(x, perm, offsets, p->E, S, p->d * esize(p->dtype),
+                                            x_perm, s),
+                    "gather launch");
+}
+
+moe_status do_gate_up(const moe_problem *p, const void *x_perm, const int32_t *offsets,
+                      const void *w1, const void *w3, void *act, hipStream_t s) {
+  const int64_t S = p->T * p->K;
+  hipError_t e;
+  if (p->dtype == MOE_F32)
+    e = moe::launch_f32_gate_up(static_cast<const float *>(x_perm), offsets,
+                                static_cast<const float *>(w1), static_cast<const float *>(w3),
+                                static_cast<float *>(act), p->E, S, int(p->d), int(p->h), s);
+  else if (resolve(p) == MOE_PATH_STREAM)
+    e = moe::launch_stream_gate_up(x_perm, offsets, w1, w3, act, p->E, int(p->d), int(p->h), p->T,
+                                   s);
+  else
+    e = moe::launch_tiled_gate_up(x_perm, offsets, w1, w3, act, p->E, S, int(p->d), int(p->h), s);
+  return hip_result(e, "gate-up launch");
+}
+
+moe_status do_down(const moe_problem *p, const void *act, const int32_t *offsets, const void *w2,
+                   float *o_perm, hipStream_t s) {
+  const int64_t S = p->T * p->K;
+  hipError_t e;
+  if (p->dtype == MOE_F32)
+    e = moe::launch_f32_down(static_cast<const float *>(act), offsets,
+                             static_cast<const float *>(w2), o_perm, p->E, S, int(p->d), int(p->h),
+                             s);
+  else if (resolve(p) == MOE_PATH_STREAM)
+    e = moe::launch_stream_down(act, offsets, w2, o_perm, p->E, int(p->d), int(p->h), p->T, s);
+  else
+    e = moe::launch_tiled_down(act, offsets, w2, o_perm, p->E, S, int(p->d), int(p->h), s);
+  return hip_result(e, "down launch");
+}
+
+moe_status do_combine(const moe_problem *p, const float *o_perm, const int32_t *slot,
+                      const float *w, void *y, hipStream_t s) {
+  return hip_result(moe::launch_combine(o_perm, slot, w, p->T, p->K, int(p->d),
+                                        p->out_dtype == MOE_BF16, y, s),
+                    "combine launch");
+}
+
+template <class F>
+moe_status guarded(F &&f) {
+  try {
+    return f();
+  } catch (const std::exception &ex) {
+    return fail(MOE_ERR_HIP, "internal error: %s", ex.what());
+  } catch (...) {
+    return fail(MOE_ERR_HIP, "internal error");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+int moe_resolve_path(const moe_problem *p) {
+  const moe_status st = check_problem(p);
+  if (st != MOE_OK) return -int(st);
+  return resolve(p);
+}
+
+moe_status moe_route(const moe_problem *p, const void *x, const void *w_g, int32_t *topk_idx,
+                     float *topk_w, float *logits, void *stream) {
+  return guarded([&] {
+    CHECK(check_problem(p));
+    CHECK(check_ptr(x, "x"));
+    CHECK(check_ptr(w_g, "w_g"));
+    CHECK(check_ptr(topk_idx, "topk_idx"));
+    CHECK(check_ptr(topk_w, "topk_w"));
+    CHECK(check_ptr(logits, "logits", false));
+    CHECK(do_route(p, x, w_g, topk_idx, topk_w, logits, as_stream(stream)));
+    return ok();
+  });
+}
+
+moe_status moe_permute(const moe_problem *p, const void *x, const int32_t *topk_idx,
+                       int32_t *offsets, int32_t *perm_token, int32_t *slot_pos, void *x_perm,
+                       void *stream) {
+  return guarded([&] {
+    CHECK(check_problem(p));
+    CHECK(check_ptr(x, "x"));
+    CHECK(check_ptr(topk_idx, "topk_idx"));
+    CHECK(check_ptr(offsets, "offsets"));
+    CHECK(check_ptr(perm_token, "perm_token"));
+    CHECK(check_ptr(slot_pos, "slot_pos"));
+    CHECK(check_ptr(x_perm, "x_perm"));
+    CHECK(do_permute(p, x, topk_idx, offsets, perm_token, slot_pos, x_perm, as_stream(stream)));
+    return ok();
+  });
+}
+
+moe_status moe_expert_gate_up(const moe_problem *p, const void *x_perm, const int32_t *offsets,
+                              const void *w1, const void *w3, void *act, void *stream) {
+  return guarded([&] {
+    CHECK(check_problem(p));
+    CHECK(check_ptr(x_perm, "x_perm"));
+    CHECK(check_ptr(offsets, "offsets"));
+    CHECK(check_ptr(w1, "w1"));
+    CHECK(check_ptr(w3, "w3"));
+    CHECK(check_ptr(act, "act"));
+    CHECK(do_gate_up(p, x_perm, offsets, w1, w3, act, as_stream(stream)));
+    return ok();
+  });
+}
+
+moe_status moe_expert_down(const moe_problem *p, const void *act, const int32_t *offsets,
+                           const void *w2, float *o_perm, void *stream) {
+  return guarded([&] {
+    CHECK(check_problem(p));
+    CHECK(check_ptr(act, "act"));
+    CHECK(check_ptr(offsets, "offsets"));
+    CHECK(check_ptr(w2, "w2"));
+    CHECK(check_ptr(o_perm, "o_perm"));
+    CHECK(do_down(p, act, offsets, w2, o_perm, as_stream(stream)));
+    return ok();
+  });
+}
+
+size_t moe_expert_workspace_bytes(const moe_problem *p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return align256(size_t(p->T) * p->K * p->h * esize(p->dtype));
+}
+
+moe_status moe_expert_swiglu(const moe_problem *p, const void *x_perm, const int32_t *offsets,
+                             const void *w1, const void *w3, const void *w2, float *o_perm,
+                             void *ws, size_t ws_bytes, void *stream) {
+  return guarded([&] {
+    CHECK(check_problem(p));
+    CHECK(check_ptr(x_perm, "x_perm"));
+    CHECK(check_ptr(offsets, "offsets"));
+    CHECK(check_ptr(w1, "w1"));
+    CHECK(check_ptr(w3, "w3"));
+    CHECK(check_ptr(w2, "w2"));
+    CHECK(check_ptr(o_perm, "o_perm"));
+    CHECK(check_ptr(ws, "ws"));
+    const size_t need = moe_expert_workspace_bytes(p);
+    if (ws_bytes < need)
+      return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    const hipStream_t s = as_stream(stream);
+    CHECK(do_gate_up(p, x_perm, offsets, w1, w3, ws, s));
+    CHECK(do_down(p, ws, offsets, w2, o_perm, s));
+    return ok();
+  });
+}
+
+moe_status moe_combine(const moe_problem *p, const float *o_perm, const int32_t *slot_pos,
+                       const float *topk_w, void *y, void *stream) {
+  return guarded([&] {
+    CHECK(check_problem(p));
+    CHECK(check_ptr(o_perm, "o_perm"));
+    CHECK(check_ptr(slot_pos, "slot_pos"));
+    CHECK(check_ptr(topk_w, "topk_w"));
+    CHECK(check_ptr(y, "y"));
+    CHECK(do_combine(p, o_perm, slot_pos, topk_w, y, as_stream(stream)));
+    return ok();
+  });
+}
+
+size_t moe_forward_workspace_bytes(const moe_problem *p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return forward_layout(p).total;
+}
+
+moe_status moe_forward(const moe_problem *p, const void *x, const void *w_g, const void *w1,
+                       const void *w3, const void *w2, void *y, int32_t *topk_idx, float *topk_w,
+                       void *ws, size_t ws_bytes, void *stream) {
+  return guarded([&] {
+    CHECK(check_problem(p));
+    CHECK(check_ptr(x, "x"));
+    CHECK(check_ptr(w_g, "w_g"));
+    CHECK(check_ptr(w1, "w1"));
+    CHECK(check_ptr(w3, "w3"));
+    CHECK(check_ptr(w2, "w2"));
+    CHECK(check_ptr(y, "y"));
+    CHECK(check_ptr(topk_idx, "topk_idx", false));
+    CHECK(check_ptr(topk_w, "topk_w", false));
+    CHECK(check_ptr(ws, "ws"));
+    if (reinterpret_cast<uintptr_t>(ws) % 256)
+      return fail(MOE_ERR_ALIGN, "ws is not 256-byte aligned");
+    const ForwardLayout L = forward_layout(p);
+    if (ws_bytes < L.total)
+      return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+    char *base = static_cast<char *>(ws);
+    int32_t *idx = topk_idx ? topk_idx : reinterpret_cast<int32_t *>(base + L.idx);
+    float *w = topk_w ? topk_w : reinterpret_cast<float *>(base + L.w);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+    int32_t *perm = reinterpret_cast<int32_t *>(base + L.perm);
+    int32_t *slot = reinterpret_cast<int32_t *>(base + L.slot);
+    void *x_perm = base + L.x_perm;
+    void *act = base + L.act;
+    float *o_perm = reinterpret_cast<float *>(base + L.o_perm);
+    const hipStream_t s = as_stream(stream);
+    CHECK(do_route(p, x, w_g, idx, w, nullptr, s));
+    CHECK(do_permute(p, x, idx, offsets, perm, slot, x_perm, s));
+    CHECK(do_gate_up(p, x_perm, offsets, w1, w3, act, s));
+    CHECK(do_down(p, act, offsets, w2, o_perm, s));
+    CHECK(do_combine(p, o_perm, slot, w, y, s));
+    return ok();
+  });
+}
+
+}  // extern "C"

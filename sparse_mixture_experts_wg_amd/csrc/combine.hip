@@ -1,0 +1,58 @@
+// combine.hip -- weighted scatter back to token order.
+//
+// y[t] = sum_k w[t, k] * o_perm[slot_pos[t, k]] (crackai page, y = w_1 Expert_i1(x)
+// + w_2 Expert_i2(x); notion page, output equation). Each token gathers its K
+// expert rows, so no two threads write the same output and no atomics are
+// needed; the K terms are added in k order with fused multiply-adds in float32
+// and the sum is rounded once to the output type.
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o_perm,
+                                                      const int32_t *__restrict__ slot_pos,
+                                                      const float *__restrict__ w, int64_t T,
+                                                      int64_t S, int K, int d, int chunks,
+                                                      void *__restrict__ y) {
+  const int64_t t = int64_t(blockIdx.x) / chunks;
+  const int col = (int(blockIdx.x % chunks) * 256 + threadIdx.x) * 4;
+  if (t >= T || col >= d) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < K; ++k) {
+    const int32_t p = slot_pos[t * K + k];
+    if (p < 0 || p >= S) continue;
+    const float wk = w[t * K + k];
+    const float4 o = *reinterpret_cast<const float4 *>(o_perm + int64_t(p) * d + col);
+    acc.x = fmaf(wk, o.x, acc.x);
+    acc.y = fmaf(wk, o.y, acc.y);
+    acc.z = fmaf(wk, o.z, acc.z);
+    acc.w = fmaf(wk, o.w, acc.w);
+  }
+  if constexpr (OUT_BF16) {
+    uint2 q;
+    q.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
+    q.y = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(y) + t * d + col) = q;
+  } else {
+    *reinterpret_cast<float4 *>(static_cast<float *>(y) + t * d + col) = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float *o_perm, const int32_t *slot_pos, const float *w, int64_t T,
+                          int K, int d, bool out_bf16, void *y, hipStream_t s) {
+  const int chunks = (d + 1023) / 1024;
+  const dim3 grid(unsigned(T * chunks));
+  if (out_bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, o_perm, slot_pos, w, T, T * K, K,
+                       d, chunks, y);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, o_perm, slot_pos, w, T, T * K, K,
+                       d, chunks, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

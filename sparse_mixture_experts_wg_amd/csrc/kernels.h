@@ -1,0 +1,60 @@
+// kernels.h -- internal launchers of the gfx950 kernels behind moe.h.
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float32 -> bf16 bits, round to nearest even (finite input).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---- router -----------------------------------------------------------------
+hipError_t launch_route(bool bf16, const void *x, const void *wg, int64_t T, int d, int E, int K,
+                        int32_t *idx, float *w, float *logits, hipStream_t s);
+
+// ---- permute ----------------------------------------------------------------
+hipError_t launch_permute_index(const int32_t *idx, int64_t S, int K, int E, int32_t *offsets,
+                                int32_t *perm_token, int32_t *slot_pos, hipStream_t s);
+hipError_t launch_gather_rows(const void *x, const int32_t *perm_token, const int32_t *offsets,
+                              int E, int64_t S, int64_t row_bytes, void *x_perm, hipStream_t s);
+
+// ---- expert projections -------------------------------------------------------
+// STREAM path (bf16; fast while every expert has <= 64 rows).
+hipError_t launch_stream_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
+                                 const void *w3, void *act, int E, int d, int h, int64_t max_rows,
+                                 hipStream_t s);
+hipError_t launch_stream_down(const void *act, const int32_t *offsets, const void *w2,
+                              float *o_perm, int E, int d, int h, int64_t max_rows, hipStream_t s);
+// TILED path (bf16 matrix cores).
+hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
+                                const void *w3, void *act, int E, int64_t S, int d, int h,
+                                hipStream_t s);
+hipError_t launch_tiled_down(const void *act, const int32_t *offsets, const void *w2,
+                             float *o_perm, int E, int64_t S, int d, int h, hipStream_t s);
+// float32 problems.
+hipError_t launch_f32_gate_up(const float *x_perm, const int32_t *offsets, const float *w1,
+                              const float *w3, float *act, int E, int64_t S, int d, int h,
+                              hipStream_t s);
+hipError_t launch_f32_down(const float *act, const int32_t *offsets, const float *w2,
+                           float *o_perm, int E, int64_t S, int d, int h, hipStream_t s);
+
+// ---- combine ----------------------------------------------------------------
+hipError_t launch_combine(const float *o_perm, const int32_t *slot_pos, const float *w, int64_t T,
+                          int K, int d, bool out_bf16, void *y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,134 @@
+// permute.hip -- gather each expert's token-slots into one contiguous segment.
+//
+// Tokens spread unevenly over the experts and have to be gathered per expert
+// before the expert matrices run and scattered back afterwards (ml-canon page,
+// "Questions worth asking"; notion page, the expert-parallel paragraph: each
+// expert's output is returned to the token's original place).
+//
+// permute_index: ONE workgroup of 1024 threads does a stable counting sort of
+// the S = T*K slots by expert id. Thread i owns the contiguous slot range
+// [i*c, (i+1)*c); it counts its slots per expert, a wavefront scan plus a scan
+// over the 16 wavefront totals gives every thread its first row per expert,
+// and a second pass over the same range assigns rows in slot order. The result
+// is the stable order (ascending s = t*K + k within an expert) with no atomics.
+// The slot index arrays are small (S int32), so one CU suffices.
+//
+// gather_rows: one wavefront per sorted row copies x[perm_token[r]] with 16-byte
+// loads/stores.
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWavesPerBlock = kThreads / 64;
+
+__global__ __launch_bounds__(kThreads) void permute_index_kernel(
+    const int32_t *__restrict__ idx, int64_t S, int K, int E, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ perm_token, int32_t *__restrict__ slot_pos) {
+  __shared__ int32_t wave_tot[kWavesPerBlock][8];
+  __shared__ int32_t wave_pre[kWavesPerBlock][8];
+  __shared__ int32_t expert_off[9];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t chunk = (S + kThreads - 1) / kThreads;
+  const int64_t s0 = min(S, int64_t(tid) * chunk);
+  const int64_t s1 = min(S, s0 + chunk);
+
+  int cnt[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) cnt[e] = 0;
+  for (int64_t s = s0; s < s1; ++s) {
+    const int e = idx[s];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) cnt[q] += (q == e && q < E) ? 1 : 0;
+  }
+
+  // inclusive scan of cnt over the lanes of the wavefront
+  int incl[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    int v = cnt[e];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(v, off, 64);
+      if (lane >= off) v += u;
+    }
+    incl[e] = v;
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wave_tot[wave][e] = incl[e];
+  }
+  __syncthreads();
+  if (tid < 8) {
+    int run = 0;
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      wave_pre[w][tid] = run;
+      run += wave_tot[w][tid];
+    }
+    wave_tot[0][tid] = run;  // expert total (wave_tot[0] is no longer needed)
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    expert_off[0] = 0;
+    for (int e = 0; e < 8; ++e) {
+      run += (e < E) ? wave_tot[0][e] : 0;
+      expert_off[e + 1] = run;
+    }
+    for (int e = 0; e <= E; ++e) offsets[e] = expert_off[e];
+  }
+  __syncthreads();
+
+  int pos[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pos[e] = expert_off[e] + wave_pre[wave][e] + incl[e] - cnt[e];
+  for (int64_t s = s0; s < s1; ++s) {
+    const int e = idx[s];
+    int p = -1;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q == e && q < E) {
+        p = pos[q];
+        pos[q] = p + 1;
+      }
+    }
+    slot_pos[s] = p;
+    if (p >= 0) perm_token[p] = int32_t(s / K);
+  }
+}
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restrict__ x,
+                                                          const int32_t *__restrict__ perm_token,
+                                                          const int32_t *__restrict__ offsets,
+                                                          int E, int64_t S, int64_t row_vecs,
+                                                          uint4 *__restrict__ x_perm) {
+  const int64_t r = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= S || r >= offsets[E]) return;
+  const int64_t t = perm_token[r];
+  const uint4 *src = x + t * row_vecs;
+  uint4 *dst = x_perm + r * row_vecs;
+  for (int64_t i = lane; i < row_vecs; i += 64) dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_permute_index(const int32_t *idx, int64_t S, int K, int E, int32_t *offsets,
+                                int32_t *perm_token, int32_t *slot_pos, hipStream_t s) {
+  hipLaunchKernelGGL(permute_index_kernel, dim3(1), dim3(kThreads), 0, s, idx, S, K, E, offsets,
+                     perm_token, slot_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void *x, const int32_t *perm_token, const int32_t *offsets,
+                              int E, int64_t S, int64_t row_bytes, void *x_perm, hipStream_t s) {
+  const dim3 grid(unsigned((S + 3) / 4));
+  hipLaunchKernelGGL(gather_rows_kernel, grid, dim3(256), 0, s, static_cast<const uint4 *>(x),
+                     perm_token, offsets, E, S, row_bytes / 16, static_cast<uint4 *>(x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,116 @@
+"""The C-ABI library without a GPU: it loads, exports what include/moe.h
+declares, and rejects invalid arguments on the host before enqueuing anything.
+
+Every call below fails validation, so no HIP call is made."""
+import ctypes
+
+import pytest
+
+import sparse_mixture_experts_wg_amd as moe
+from sparse_mixture_experts_wg_amd import binding
+
+lib = moe.lib
+FAKE = 1 << 20  # aligned, never dereferenced (validation fails first)
+
+
+def _p(**kw):
+    base = dict(T=64, d=256, h=384, E=8, K=2, dtype="bf16", out_dtype="f32", path="auto")
+    base.update(kw)
+    return moe.problem(**base)
+
+
+def test_exports_every_declared_function():
+    names = moe.header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    for required in ("moe_route", "moe_permute", "moe_expert_swiglu", "moe_combine", "moe_forward"):
+        assert required in names
+
+
+def test_status_strings():
+    assert moe.status_string(0) == "MOE_OK"
+    assert moe.status_string(5) == "MOE_ERR_WORKSPACE"
+    assert moe.status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), binding.ERR_SHAPE),
+    (dict(d=0), binding.ERR_SHAPE),
+    (dict(E=2, K=3), binding.ERR_SHAPE),
+    (dict(E=9), binding.ERR_UNSUPPORTED),
+    (dict(E=8, K=3), binding.ERR_UNSUPPORTED),
+    (dict(d=192), binding.ERR_UNSUPPORTED),
+    (dict(h=200), binding.ERR_UNSUPPORTED),
+    (dict(dtype="f32", path="stream"), binding.ERR_UNSUPPORTED),
+    (dict(T=1 << 31), binding.ERR_UNSUPPORTED),
+])
+def test_problem_validation(kw, code):
+    p = _p(**kw)
+    assert moe.resolve_path(p) == -code
+    assert moe.forward_workspace_bytes(p) == 0
+    st = lib.moe_route(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == code, moe.last_error()
+    assert moe.last_error()
+
+
+def test_bad_dtype_and_reserved():
+    p = _p()
+    p.dtype = 7
+    assert moe.resolve_path(p) == -binding.ERR_UNSUPPORTED
+    p = _p()
+    p.reserved = 1
+    assert moe.resolve_path(p) == -binding.ERR_UNSUPPORTED
+    p = _p()
+    p.path = 5
+    assert moe.resolve_path(p) == -binding.ERR_UNSUPPORTED
+
+
+def test_path_resolution():
+    assert moe.resolve_path(_p(T=64)) == binding.PATH_STREAM
+    assert moe.resolve_path(_p(T=65)) == binding.PATH_TILED
+    assert moe.resolve_path(_p(T=4096, path="stream")) == binding.PATH_STREAM
+    assert moe.resolve_path(_p(T=8, path="tiled")) == binding.PATH_TILED
+    assert moe.resolve_path(_p(dtype="f32")) == binding.PATH_TILED
+
+
+def test_null_and_alignment():
+    p = _p()
+    assert lib.moe_route(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, None) == binding.ERR_NULL
+    assert "x" in moe.last_error()
+    assert lib.moe_route(None, FAKE, FAKE, FAKE, FAKE, None, None) == binding.ERR_NULL
+    assert lib.moe_route(ctypes.byref(p), FAKE + 8, FAKE, FAKE, FAKE, None, None) == binding.ERR_ALIGN
+    assert lib.moe_combine(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE + 4, None) == binding.ERR_ALIGN
+    assert lib.moe_permute(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == binding.ERR_NULL
+    assert lib.moe_expert_gate_up(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, None) == binding.ERR_NULL
+    assert lib.moe_expert_down(ctypes.byref(p), FAKE, FAKE, None, FAKE, None) == binding.ERR_NULL
+
+
+def test_workspace_sizes_and_too_small():
+    p = _p(T=100, d=256, h=512, E=8, K=2)
+    S = 200
+    need = moe.forward_workspace_bytes(p)
+    # x_perm + act (bf16) + o_perm (f32) + 4 int/float index arrays + offsets, 256-B aligned
+    assert need >= S * 256 * 2 + S * 512 * 2 + S * 256 * 4 + 4 * S * 4
+    assert need % 256 == 0
+    assert moe.expert_workspace_bytes(p) == S * 512 * 2
+    st = lib.moe_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                         need - 1, None)
+    assert st == binding.ERR_WORKSPACE, moe.last_error()
+    st = lib.moe_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                         FAKE + 16, need, None)
+    assert st == binding.ERR_ALIGN  # ws must be 256-byte aligned
+    st = lib.moe_expert_swiglu(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               moe.expert_workspace_bytes(p) - 1, None)
+    assert st == binding.ERR_WORKSPACE
+    f32 = _p(T=100, d=256, h=512, dtype="f32")
+    assert moe.expert_workspace_bytes(f32) == S * 512 * 4
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    p = _p(T=4, d=128, h=128)
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.route(p, x, torch.zeros((128, 8), dtype=torch.bfloat16),
+                  topk_idx=x, topk_w=x)
