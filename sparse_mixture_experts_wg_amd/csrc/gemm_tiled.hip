@@ -86,27 +86,26 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t *__restrict__
   __shared__ __attribute__((aligned(16))) uint16_t sX[2][BT * kStride];
 
   // ---- global load assignment: thread owns 16-byte chunk (tid & 7) of rows
-  //      (tid >> 3) + 32 j
+  //      (tid >> 3) + 32 j of both tiles. Addresses are 32-bit element offsets
+  //      from wave-uniform bases (the expert's matrices, the tile's first row).
   const int kc = (tid & 7) * 8;
   const int rbase = tid >> 3;
   constexpr int kWL = kBW / 32;  // weight rows per thread
   constexpr int kXL = BT / 32;   // token rows per thread
-  const uint16_t *wsrc[kWL];
-  const uint16_t *xsrc[kXL];
-  const size_t ebase = size_t(e) * N;
+  const size_t mat_elems = size_t(N) * K;
+  const uint16_t *wa_e = Wa + size_t(e) * mat_elems;
+  const uint16_t *wb_e = GATEUP ? Wb + size_t(e) * mat_elems : wa_e;
+  const uint16_t *x_t = X + size_t(row0 + m0) * K;
+  uint32_t woff[kWL], xoff[kXL];
 #pragma unroll
   for (int j = 0; j < kWL; ++j) {
     const uint16_t *mat;
     const int row = weight_row<GATEUP>(rbase + 32 * j, c0, N, Wa, Wb, mat);
-    wsrc[j] = mat + (ebase + row) * size_t(K) + kc;
+    woff[j] = uint32_t(row) * uint32_t(K) + kc;
   }
 #pragma unroll
-  for (int j = 0; j < kXL; ++j) {
-    const int tr = min(m0 + rbase + 32 * j, ne - 1);
-    xsrc[j] = X + size_t(row0 + tr) * K + kc;
-  }
-
-  u32x4 wreg[kWL], xreg[kXL];
+  for (int j = 0; j < kXL; ++j)
+    xoff[j] = uint32_t(min(rbase + 32 * j, ne - 1 - m0)) * uint32_t(K) + kc;
 
   f32x16 acc[4][kTF];
 #pragma unroll
@@ -116,67 +115,97 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t *__restrict__
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[f][t][i] = 0.f;
 
-  // token fragments of this wavefront that hold at least one real row
-  const int tvalid = min(kTF, max(0, (ne - m0 - wc * (BT / 2) + 31) / 32));
-
   // fragment read offsets: lane reads row (lane & 31), k half (lane >> 5)
   const int frow = lane & 31;
   const int fk = (lane >> 5) * 8;
+  const uint16_t *aW = &sW[0][(wr * 128 + frow) * kStride + fk];
+  const uint16_t *aX = &sX[0][(wc * (BT / 2) + frow) * kStride + fk];
+  uint16_t *dW = &sW[0][rbase * kStride + kc];
+  uint16_t *dX = &sX[0][rbase * kStride + kc];
 
+  // Software pipeline: k-block kt+2 is fetched into registers while k-block kt
+  // is multiplied from LDS stage kt & 1 and k-block kt+1 (fetched one iteration
+  // earlier) is written into the other stage; one barrier per k-block. Blocks
+  // past the end are clamped re-reads of the last one, written to a stage that
+  // is never read again. All 4 x kTF fragments are multiplied in every k-block
+  // (no data-dependent branch touches the accumulators, so they stay in AGPRs);
+  // token rows past the expert's end are clamped duplicates whose results are
+  // never stored. K is a multiple of 128, so the k-block count is even.
+  u32x4 r0w[kWL], r0x[kXL], r1w[kWL], r1x[kXL];
   const int nk = K / kBK;
-  {
-#pragma unroll
-    for (int j = 0; j < kWL; ++j) wreg[j] = *reinterpret_cast<const u32x4 *>(wsrc[j] + 0);
-#pragma unroll
-    for (int j = 0; j < kXL; ++j) xreg[j] = *reinterpret_cast<const u32x4 *>(xsrc[j] + 0);
-#pragma unroll
-    for (int j = 0; j < kWL; ++j)
-      *reinterpret_cast<u32x4 *>(&sW[0][(rbase + 32 * j) * kStride + kc]) = wreg[j];
-#pragma unroll
-    for (int j = 0; j < kXL; ++j)
-      *reinterpret_cast<u32x4 *>(&sX[0][(rbase + 32 * j) * kStride + kc]) = xreg[j];
+#define MOE_GLOAD(RW, RX, KB)                                                                 \
+  {                                                                                           \
+    const uint32_t k0 = uint32_t(min(KB, nk - 1) * kBK);                                      \
+    _Pragma("unroll") for (int j = 0; j < kWL; ++j) {                                         \
+      const uint16_t *base = (GATEUP && ((j >> 1) & 1)) ? wb_e : wa_e;                        \
+      RW[j] = *reinterpret_cast<const u32x4 *>(base + woff[j] + k0);                          \
+    }                                                                                         \
+    _Pragma("unroll") for (int j = 0; j < kXL; ++j)                                           \
+      RX[j] = *reinterpret_cast<const u32x4 *>(x_t + xoff[j] + k0);                           \
   }
+#define MOE_SSTORE(RW, RX, ST)                                                                \
+  {                                                                                           \
+    _Pragma("unroll") for (int j = 0; j < kWL; ++j)                                           \
+      *reinterpret_cast<u32x4 *>(dW + (ST) * (kBW * kStride) + 32 * j * kStride) = RW[j];     \
+    _Pragma("unroll") for (int j = 0; j < kXL; ++j)                                           \
+      *reinterpret_cast<u32x4 *>(dX + (ST) * (BT * kStride) + 32 * j * kStride) = RX[j];      \
+  }
+// One k-block from LDS stage ST, in fenced blocks so that the order below is
+// the order issued: (global loads for block kt+2, fragments of k-step 0),
+// then per k-step: fragments of the next k-step, half of the LDS writes of
+// block kt+1 (last two k-steps), and the 4 x kTF MFMAs of this k-step. A
+// fragment read thus has a whole k-step of MFMAs to land, and the LDS writes
+// come one iteration after their global loads were issued.
+#define MOE_MMA_STAGE(ST, GLOAD_STMT, RW, RX, WST)                                            \
+  {                                                                                           \
+    const uint16_t *pw = aW + (ST) * (kBW * kStride);                                         \
+    const uint16_t *px = aX + (ST) * (BT * kStride);                                          \
+    bf16x8 fa[2][4], fb[2][kTF];                                                              \
+    GLOAD_STMT                                                                                \
+    _Pragma("unroll") for (int f = 0; f < 4; ++f)                                             \
+      fa[0][f] = *reinterpret_cast<const bf16x8 *>(pw + f * 32 * kStride);                    \
+    _Pragma("unroll") for (int t = 0; t < kTF; ++t)                                           \
+      fb[0][t] = *reinterpret_cast<const bf16x8 *>(px + t * 32 * kStride);                    \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    _Pragma("unroll") for (int kk = 0; kk < kBK / 16; ++kk) {                                 \
+      const int cur = kk & 1;                                                                 \
+      if (kk + 1 < kBK / 16) {                                                                \
+        _Pragma("unroll") for (int f = 0; f < 4; ++f) fa[cur ^ 1][f] =                        \
+            *reinterpret_cast<const bf16x8 *>(pw + f * 32 * kStride + (kk + 1) * 16);         \
+        _Pragma("unroll") for (int t = 0; t < kTF; ++t) fb[cur ^ 1][t] =                      \
+            *reinterpret_cast<const bf16x8 *>(px + t * 32 * kStride + (kk + 1) * 16);         \
+      }                                                                                       \
+      if (kk == kBK / 16 - 2) {                                                               \
+        _Pragma("unroll") for (int j = 0; j < kWL; ++j)                                       \
+          *reinterpret_cast<u32x4 *>(dW + (WST) * (kBW * kStride) + 32 * j * kStride) = RW[j]; \
+      }                                                                                       \
+      if (kk == kBK / 16 - 1) {                                                               \
+        _Pragma("unroll") for (int j = 0; j < kXL; ++j)                                       \
+          *reinterpret_cast<u32x4 *>(dX + (WST) * (BT * kStride) + 32 * j * kStride) = RX[j]; \
+      }                                                                                       \
+      __builtin_amdgcn_sched_group_barrier(0x180, 64, 1);                                     \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * kTF, 1);                                \
+      _Pragma("unroll") for (int t = 0; t < kTF; ++t)                                         \
+        _Pragma("unroll") for (int f = 0; f < 4; ++f)                                         \
+          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][f], fb[cur][t],         \
+                                                              acc[f][t], 0, 0, 0);            \
+      __builtin_amdgcn_sched_barrier(0);                                                      \
+    }                                                                                         \
+  }
+
+  MOE_GLOAD(r0w, r0x, 0)
+  MOE_GLOAD(r1w, r1x, 1)
+  MOE_SSTORE(r0w, r0x, 0)
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) {
-      const int k0 = (kt + 1) * kBK;
-#pragma unroll
-    for (int j = 0; j < kWL; ++j) wreg[j] = *reinterpret_cast<const u32x4 *>(wsrc[j] + k0);
-  #pragma unroll
-    for (int j = 0; j < kXL; ++j) xreg[j] = *reinterpret_cast<const u32x4 *>(xsrc[j] + k0);
-    }
-    if (tvalid > 0) {
-#pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        bf16x8 a[4], bx[kTF];
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-          a[f] = *reinterpret_cast<const bf16x8 *>(
-              &sW[st][(wr * 128 + f * 32 + frow) * kStride + kk * 16 + fk]);
-#pragma unroll
-        for (int t = 0; t < kTF; ++t)
-          bx[t] = *reinterpret_cast<const bf16x8 *>(
-              &sX[st][(wc * (BT / 2) + t * 32 + frow) * kStride + kk * 16 + fk]);
-#pragma unroll
-        for (int t = 0; t < kTF; ++t) {
-          if (t >= tvalid) continue;
-#pragma unroll
-          for (int f = 0; f < 4; ++f)
-            acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f], bx[t], acc[f][t], 0, 0, 0);
-        }
-      }
-    }
-    if (kt + 1 < nk) {
-#pragma unroll
-    for (int j = 0; j < kWL; ++j)
-      *reinterpret_cast<u32x4 *>(&sW[st ^ 1][(rbase + 32 * j) * kStride + kc]) = wreg[j];
-#pragma unroll
-    for (int j = 0; j < kXL; ++j)
-      *reinterpret_cast<u32x4 *>(&sX[st ^ 1][(rbase + 32 * j) * kStride + kc]) = xreg[j];
-    }
+  for (int kt = 0; kt < nk; kt += 2) {
+    MOE_MMA_STAGE(0, MOE_GLOAD(r0w, r0x, kt + 2), r1w, r1x, 1)
+    __syncthreads();
+    MOE_MMA_STAGE(1, MOE_GLOAD(r1w, r1x, kt + 3), r0w, r0x, 0)
     __syncthreads();
   }
+#undef MOE_GLOAD
+#undef MOE_SSTORE
+#undef MOE_MMA_STAGE
 
   // ---- epilogue. 32x32 accumulator: lane holds token column j = lane & 31 and
   // weight rows i = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4), r = 0..15.
