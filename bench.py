@@ -46,7 +46,28 @@ def parse():
                     help="approximate budget of the CPU-oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "stream", "tiled"])
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (steps "
+                         "times): the reference kernel for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def copy_probe(mib: int, steps: int):
+    import torch
+
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_probe_mib": mib, "read_bytes": n * 4, "write_bytes": n * 4,
+                      "ms_per_copy": round(dt * 1e3, 4),
+                      "GBps_read_plus_write": round(2 * n * 4 / dt / 1e9, 1)}), flush=True)
+    return 0
 
 
 def source_hash(files):
@@ -80,6 +101,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this layer has no "
               "multi-GPU path", file=sys.stderr)
         return 2
+
+    if args.copy_probe_mib:
+        return copy_probe(args.copy_probe_mib, max(1, args.steps))
 
     import numpy as np
     import torch

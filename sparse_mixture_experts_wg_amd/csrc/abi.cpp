@@ -49,6 +49,9 @@ moe_status check_problem(const moe_problem *p) {
   if (p->d > kMaxDim || p->h > kMaxDim)
     return fail(MOE_ERR_UNSUPPORTED, "d=%lld h=%lld: at most 2^20", (long long)p->d,
                 (long long)p->h);
+  if (p->h * p->d > kMaxIndex)
+    return fail(MOE_ERR_UNSUPPORTED, "h*d=%lld: one expert matrix must stay below 2^31 elements",
+                (long long)(p->h * p->d));
   if (p->T > kMaxIndex / p->K || p->T > kMaxIndex / ((p->d + 1023) / 1024))
     return fail(MOE_ERR_UNSUPPORTED, "T=%lld too large for 32-bit slot indices", (long long)p->T);
   if ((p->dtype != MOE_F32 && p->dtype != MOE_BF16) ||

@@ -7,13 +7,19 @@
 // the sparse-matmul kernels the pages cite are prior art, this is a plain
 // grouped GEMM over the per-expert segments).
 //
-// Tile: 256 weight rows (MFMA M side) x BT tokens (MFMA N side) x 64 k.
-//  * 4 wavefronts in a 2 x 2 grid; each owns 128 weight rows x BT/2 tokens as
-//    4 x (BT/64) accumulators of v_mfma_f32_32x32x16_bf16 (16 fp32 each).
-//  * Global -> VGPR -> LDS, two LDS stages (the next k-block's global loads are
-//    in flight while the current one is multiplied), one barrier per k-block.
-//    LDS rows are padded to 144 bytes so the 16-byte fragment reads of 8
-//    consecutive rows hit distinct banks.
+// Tile: 256 weight rows (MFMA M side) x 256 tokens (MFMA N side) x 64 k.
+//  * 8 wavefronts (2 per SIMD) in a 2 x 4 grid; each owns 128 weight rows x 64
+//    tokens as 4 x 2 accumulators of v_mfma_f32_32x32x16_bf16. Two wavefronts
+//    per SIMD keep the matrix pipe fed while the other waits on LDS or a barrier
+//    (one wavefront per SIMD tops out near 80% of the matrix peak on gfx950).
+//  * Global memory goes straight to LDS (global_load_lds_dwordx4: a wavefront
+//    instruction fills one contiguous kilobyte, lane L the bytes [16L, 16L+16)),
+//    two stages of 64 KiB; the k-block after the current one is in flight while
+//    the current one is multiplied; one barrier per k-block.
+//  * LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by
+//    (r ^ r >> 3) & 7 of the row's position in its 32-row group, so both the
+//    DMA writes and the fragment reads of 8 or 16 consecutive rows hit distinct
+//    banks (measured: zero bank conflicts).
 //  * Gate-up: the 256 weight rows are W1 and W3 rows of the same 128 output
 //    columns, interleaved in blocks of 64 so that every wavefront holds g and u
 //    of the same columns and applies silu(g) * u in registers; the result is
@@ -22,42 +28,31 @@
 //    fastest, so concurrently running tiles share weight tiles; the linear tile
 //    id is remapped so that each of the 8 XCDs (workgroups are dealt to XCDs
 //    round-robin) owns one contiguous range of tiles and its own L2 sees the
-//    reuse. Token blocks past an expert's last row skip their MFMAs.
+//    reuse. Token rows past an expert's end are clamped duplicates whose results
+//    are never stored.
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int kBW = 256;        // weight rows per tile
-constexpr int kBK = 64;         // k per stage
-constexpr int kStride = 72;     // LDS row stride in bf16 (64 + 8 padding)
 constexpr int kXCD = 8;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate with vmcnt(0) and the other counters at their maximum.
+constexpr int kWaitVm0 = 0x0F70;
+
+// Physical 16-byte chunk = logical chunk ^ swz(row); depends on row & 31 only.
+__device__ __forceinline__ int swz(int r) { return ((r & 31) ^ ((r & 31) >> 3)) & 7; }
 
 template <bool GATEUP>
-__device__ __forceinline__ int weight_row(int r, int c0, int N, const uint16_t *Wa,
-                                          const uint16_t *Wb, const uint16_t *&mat) {
-  if constexpr (GATEUP) {
-    // [0,64) W1 c0+[0,64) | [64,128) W3 c0+[0,64) | [128,192) W1 c0+64+[0,64) | [192,256) W3
-    const int blk = r >> 6;
-    mat = (blk & 1) ? Wb : Wa;
-    return min(c0 + ((blk >> 1) << 6) + (r & 63), N - 1);
-  } else {
-    mat = Wa;
-    return min(c0 + r, N - 1);
-  }
-}
-
-template <bool GATEUP, int BT>
-__global__ __launch_bounds__(256) void tiled_kernel(const uint16_t *__restrict__ X,
-                                                    const int32_t *__restrict__ offsets, int E,
-                                                    const uint16_t *__restrict__ Wa,
-                                                    const uint16_t *__restrict__ Wb,
-                                                    void *__restrict__ out, int N, int K) {
-  constexpr int kCols = GATEUP ? kBW / 2 : kBW;  // output columns per tile
-  constexpr int kTF = BT / 64;                   // token fragments (32 wide) per wavefront
-  const int ct = (N + kCols - 1) / kCols;        // column blocks per expert
-
-  // ---- which tile: total over experts, XCD-aware remap --------------------
+__global__ __launch_bounds__(512) void tiled_kernel(const uint16_t *__restrict__ X,
+                                                     const int32_t *__restrict__ offsets, int E,
+                                                     const uint16_t *__restrict__ Wa,
+                                                     const uint16_t *__restrict__ Wb,
+                                                     void *__restrict__ out, int N, int K) {
+  constexpr int BT = 256;
+  constexpr int kCols = GATEUP ? 128 : 256;
+  const int ct = (N + kCols - 1) / kCols;
   int total = 0;
   for (int q = 0; q < E; ++q) total += ct * ((offsets[q + 1] - offsets[q] + BT - 1) / BT);
   const int g8 = (total + kXCD - 1) / kXCD;
@@ -80,139 +75,112 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t *__restrict__
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> 2, wc = wave & 3;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kBW * kStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][BT * kStride];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW0[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX0[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX1[256 * 64];
 
-  // ---- global load assignment: thread owns 16-byte chunk (tid & 7) of rows
-  //      (tid >> 3) + 32 j of both tiles. Addresses are 32-bit element offsets
-  //      from wave-uniform bases (the expert's matrices, the tile's first row).
-  const int kc = (tid & 7) * 8;
-  const int rbase = tid >> 3;
-  constexpr int kWL = kBW / 32;  // weight rows per thread
-  constexpr int kXL = BT / 32;   // token rows per thread
+  // ---- DMA assignment: wave w fills rows [32w, 32w+32) of both tiles, 8 rows per
+  // instruction; lane p writes LDS bytes [16p, 16p+16) of the instruction's
+  // kilobyte: row 8i + p/8, physical chunk p%8 = logical chunk ^ swz(row).
   const size_t mat_elems = size_t(N) * K;
-  const uint16_t *wa_e = Wa + size_t(e) * mat_elems;
-  const uint16_t *wb_e = GATEUP ? Wb + size_t(e) * mat_elems : wa_e;
+  const uint16_t *wmat = Wa + size_t(e) * mat_elems;
+  if (GATEUP && ((wave >> 1) & 1)) wmat = Wb + size_t(e) * mat_elems;
   const uint16_t *x_t = X + size_t(row0 + m0) * K;
-  uint32_t woff[kWL], xoff[kXL];
+  uint32_t wofs[4], xofs[4];
 #pragma unroll
-  for (int j = 0; j < kWL; ++j) {
-    const uint16_t *mat;
-    const int row = weight_row<GATEUP>(rbase + 32 * j, c0, N, Wa, Wb, mat);
-    woff[j] = uint32_t(row) * uint32_t(K) + kc;
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 32 + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    int wrow;
+    if constexpr (GATEUP) wrow = c0 + ((r >> 7) << 6) + (r & 63);
+    else wrow = min(c0 + r, N - 1);
+    wofs[i] = uint32_t(wrow) * uint32_t(K) + c * 8;
+    xofs[i] = uint32_t(min(r, ne - 1 - m0)) * uint32_t(K) + c * 8;
   }
-#pragma unroll
-  for (int j = 0; j < kXL; ++j)
-    xoff[j] = uint32_t(min(rbase + 32 * j, ne - 1 - m0)) * uint32_t(K) + kc;
+  const int dma_row = wave * 32;
 
-  f32x16 acc[4][kTF];
+  // ---- fragment read addresses (bytes): row (lane & 31) of a 32-row group,
+  // logical chunk kk*2 + (lane >> 5)
+  const int g = (lane >> 5) ^ swz(lane & 31);
+  uint32_t offk[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) offk[kk] = uint32_t(((kk * 2) ^ g) * 16);
+  const uint32_t baseA = uint32_t((wr * 128 + (lane & 31)) * 128);
+  const uint32_t baseB = uint32_t((wc * 64 + (lane & 31)) * 128);
+
+  f32x16 acc[4][2];
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int t = 0; t < kTF; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[f][t][i] = 0.f;
 
-  // fragment read offsets: lane reads row (lane & 31), k half (lane >> 5)
-  const int frow = lane & 31;
-  const int fk = (lane >> 5) * 8;
-  const uint16_t *aW = &sW[0][(wr * 128 + frow) * kStride + fk];
-  const uint16_t *aX = &sX[0][(wc * (BT / 2) + frow) * kStride + fk];
-  uint16_t *dW = &sW[0][rbase * kStride + kc];
-  uint16_t *dX = &sX[0][rbase * kStride + kc];
+  const int nk = K / 64;
 
-  // Software pipeline: k-block kt+2 is fetched into registers while k-block kt
-  // is multiplied from LDS stage kt & 1 and k-block kt+1 (fetched one iteration
-  // earlier) is written into the other stage; one barrier per k-block. Blocks
-  // past the end are clamped re-reads of the last one, written to a stage that
-  // is never read again. All 4 x kTF fragments are multiplied in every k-block
-  // (no data-dependent branch touches the accumulators, so they stay in AGPRs);
-  // token rows past the expert's end are clamped duplicates whose results are
-  // never stored. K is a multiple of 128, so the k-block count is even.
-  u32x4 r0w[kWL], r0x[kXL], r1w[kWL], r1x[kXL];
-  const int nk = K / kBK;
-#define MOE_GLOAD(RW, RX, KB)                                                                 \
-  {                                                                                           \
-    const uint32_t k0 = uint32_t(min(KB, nk - 1) * kBK);                                      \
-    _Pragma("unroll") for (int j = 0; j < kWL; ++j) {                                         \
-      const uint16_t *base = (GATEUP && ((j >> 1) & 1)) ? wb_e : wa_e;                        \
-      RW[j] = *reinterpret_cast<const u32x4 *>(base + woff[j] + k0);                          \
-    }                                                                                         \
-    _Pragma("unroll") for (int j = 0; j < kXL; ++j)                                           \
-      RX[j] = *reinterpret_cast<const u32x4 *>(x_t + xoff[j] + k0);                           \
+#define DMA(SW, SX, KB)                                                                    \
+  {                                                                                        \
+    const uint32_t k0 = uint32_t(min(KB, nk - 1) * 64);                                    \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                        \
+      __builtin_amdgcn_global_load_lds(wmat + wofs[i] + k0,                                \
+                                       (lds_void *)(SW + (dma_row + i * 8) * 64), 16, 0, 0); \
+      __builtin_amdgcn_global_load_lds(x_t + xofs[i] + k0,                                 \
+                                       (lds_void *)(SX + (dma_row + i * 8) * 64), 16, 0, 0); \
+    }                                                                                      \
   }
-#define MOE_SSTORE(RW, RX, ST)                                                                \
-  {                                                                                           \
-    _Pragma("unroll") for (int j = 0; j < kWL; ++j)                                           \
-      *reinterpret_cast<u32x4 *>(dW + (ST) * (kBW * kStride) + 32 * j * kStride) = RW[j];     \
-    _Pragma("unroll") for (int j = 0; j < kXL; ++j)                                           \
-      *reinterpret_cast<u32x4 *>(dX + (ST) * (BT * kStride) + 32 * j * kStride) = RX[j];      \
-  }
-// One k-block from LDS stage ST, in fenced blocks so that the order below is
-// the order issued: (global loads for block kt+2, fragments of k-step 0),
-// then per k-step: fragments of the next k-step, half of the LDS writes of
-// block kt+1 (last two k-steps), and the 4 x kTF MFMAs of this k-step. A
-// fragment read thus has a whole k-step of MFMAs to land, and the LDS writes
-// come one iteration after their global loads were issued.
-#define MOE_MMA_STAGE(ST, GLOAD_STMT, RW, RX, WST)                                            \
-  {                                                                                           \
-    const uint16_t *pw = aW + (ST) * (kBW * kStride);                                         \
-    const uint16_t *px = aX + (ST) * (BT * kStride);                                          \
-    bf16x8 fa[2][4], fb[2][kTF];                                                              \
-    GLOAD_STMT                                                                                \
-    _Pragma("unroll") for (int f = 0; f < 4; ++f)                                             \
-      fa[0][f] = *reinterpret_cast<const bf16x8 *>(pw + f * 32 * kStride);                    \
-    _Pragma("unroll") for (int t = 0; t < kTF; ++t)                                           \
-      fb[0][t] = *reinterpret_cast<const bf16x8 *>(px + t * 32 * kStride);                    \
-    __builtin_amdgcn_sched_barrier(0);                                                        \
-    _Pragma("unroll") for (int kk = 0; kk < kBK / 16; ++kk) {                                 \
-      const int cur = kk & 1;                                                                 \
-      if (kk + 1 < kBK / 16) {                                                                \
-        _Pragma("unroll") for (int f = 0; f < 4; ++f) fa[cur ^ 1][f] =                        \
-            *reinterpret_cast<const bf16x8 *>(pw + f * 32 * kStride + (kk + 1) * 16);         \
-        _Pragma("unroll") for (int t = 0; t < kTF; ++t) fb[cur ^ 1][t] =                      \
-            *reinterpret_cast<const bf16x8 *>(px + t * 32 * kStride + (kk + 1) * 16);         \
-      }                                                                                       \
-      if (kk == kBK / 16 - 2) {                                                               \
-        _Pragma("unroll") for (int j = 0; j < kWL; ++j)                                       \
-          *reinterpret_cast<u32x4 *>(dW + (WST) * (kBW * kStride) + 32 * j * kStride) = RW[j]; \
-      }                                                                                       \
-      if (kk == kBK / 16 - 1) {                                                               \
-        _Pragma("unroll") for (int j = 0; j < kXL; ++j)                                       \
-          *reinterpret_cast<u32x4 *>(dX + (WST) * (BT * kStride) + 32 * j * kStride) = RX[j]; \
-      }                                                                                       \
-      __builtin_amdgcn_sched_group_barrier(0x180, 64, 1);                                     \
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * kTF, 1);                                \
-      _Pragma("unroll") for (int t = 0; t < kTF; ++t)                                         \
-        _Pragma("unroll") for (int f = 0; f < 4; ++f)                                         \
-          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][f], fb[cur][t],         \
-                                                              acc[f][t], 0, 0, 0);            \
-      __builtin_amdgcn_sched_barrier(0);                                                      \
-    }                                                                                         \
+#define COMPUTE(SW, SX)                                                                    \
+  {                                                                                        \
+    const char *pa = reinterpret_cast<const char *>(SW) + baseA;                           \
+    const char *pb = reinterpret_cast<const char *>(SX) + baseB;                           \
+    bf16x8 fa[2][4], fb[2][2];                                                             \
+    _Pragma("unroll") for (int f = 0; f < 4; ++f)                                          \
+      fa[0][f] = *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[0]);               \
+    _Pragma("unroll") for (int t = 0; t < 2; ++t)                                          \
+      fb[0][t] = *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[0]);               \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                     \
+      const int cur = kk & 1;                                                              \
+      if (kk + 1 < 4) {                                                                    \
+        _Pragma("unroll") for (int f = 0; f < 4; ++f) fa[cur ^ 1][f] =                     \
+            *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[kk + 1]);               \
+        _Pragma("unroll") for (int t = 0; t < 2; ++t) fb[cur ^ 1][t] =                     \
+            *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[kk + 1]);               \
+      }                                                                                    \
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);                                   \
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);                                   \
+      _Pragma("unroll") for (int t = 0; t < 2; ++t)                                        \
+        _Pragma("unroll") for (int f = 0; f < 4; ++f)                                      \
+          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][f], fb[cur][t],      \
+                                                              acc[f][t], 0, 0, 0);         \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+    }                                                                                      \
   }
 
-  MOE_GLOAD(r0w, r0x, 0)
-  MOE_GLOAD(r1w, r1x, 1)
-  MOE_SSTORE(r0w, r0x, 0)
+  DMA(sW0, sX0, 0)
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
-    MOE_MMA_STAGE(0, MOE_GLOAD(r0w, r0x, kt + 2), r1w, r1x, 1)
+    DMA(sW1, sX1, kt + 1)
+    COMPUTE(sW0, sX0)
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    MOE_MMA_STAGE(1, MOE_GLOAD(r1w, r1x, kt + 3), r0w, r0x, 0)
+    DMA(sW0, sX0, kt + 2)
+    COMPUTE(sW1, sX1)
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   }
-#undef MOE_GLOAD
-#undef MOE_SSTORE
-#undef MOE_MMA_STAGE
+#undef DMA
+#undef COMPUTE
 
-  // ---- epilogue. 32x32 accumulator: lane holds token column j = lane & 31 and
-  // weight rows i = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4), r = 0..15.
+  // ---- epilogue: lane holds token column j = lane & 31 and weight rows
+  // i = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4) of each 32x32 fragment.
   const int ih = 4 * (lane >> 5);
 #pragma unroll
-  for (int t = 0; t < kTF; ++t) {
-    const int tok = m0 + wc * (BT / 2) + t * 32 + (lane & 31);
+  for (int t = 0; t < 2; ++t) {
+    const int tok = m0 + wc * 64 + t * 32 + (lane & 31);
     if (tok >= ne) continue;
     const size_t orow = size_t(row0 + tok) * N;
     if constexpr (GATEUP) {
@@ -247,31 +215,28 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t *__restrict__
   }
 }
 
-constexpr int kBTGateUp = 256;
-constexpr int kBTDown = 256;
-
 // Upper bound of the tile count for any split of S rows over E experts.
-inline unsigned tiled_grid(int64_t S, int E, int N, int cols, int BT) {
+inline unsigned tiled_grid(int64_t S, int E, int N, int cols) {
   const int64_t ct = (N + cols - 1) / cols;
-  const int64_t tiles = ct * ((S + BT - 1) / BT + E);
+  const int64_t tiles = ct * ((S + 255) / 256 + E);
   return unsigned((tiles + kXCD - 1) / kXCD * kXCD);
 }
 
 }  // namespace
 
 hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
-                                const void *w3, void *act, int E, int64_t S, int d, int h,
-                                hipStream_t s) {
-  hipLaunchKernelGGL((tiled_kernel<true, kBTGateUp>), dim3(tiled_grid(S, E, h, kBW / 2, kBTGateUp)),
-                     dim3(256), 0, s, static_cast<const uint16_t *>(x_perm), offsets, E,
+                                 const void *w3, void *act, int E, int64_t S, int d, int h,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL((tiled_kernel<true>), dim3(tiled_grid(S, E, h, 128)), dim3(512), 0, s,
+                     static_cast<const uint16_t *>(x_perm), offsets, E,
                      static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3), act, h, d);
   return hipGetLastError();
 }
 
 hipError_t launch_tiled_down(const void *act, const int32_t *offsets, const void *w2,
-                             float *o_perm, int E, int64_t S, int d, int h, hipStream_t s) {
-  hipLaunchKernelGGL((tiled_kernel<false, kBTDown>), dim3(tiled_grid(S, E, d, kBW, kBTDown)),
-                     dim3(256), 0, s, static_cast<const uint16_t *>(act), offsets, E,
+                              float *o_perm, int E, int64_t S, int d, int h, hipStream_t s) {
+  hipLaunchKernelGGL((tiled_kernel<false>), dim3(tiled_grid(S, E, d, 256)), dim3(512), 0, s,
+                     static_cast<const uint16_t *>(act), offsets, E,
                      static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(nullptr),
                      static_cast<void *>(o_perm), d, h);
   return hipGetLastError();
