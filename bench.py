@@ -204,17 +204,22 @@ def main():
     sha = source_hash(kernel_files(path)) if path != "f32" else None
     traffic_rec = load_traffic(cfg.name, kernel, sha) if sha else None
     traffic = None
+    traffic_detail = None
     if traffic_rec:
-        traffic = {"fetch_bytes": traffic_rec["fetch_bytes_per_launch"],
-                   "write_bytes": traffic_rec["write_bytes_per_launch"],
-                   "source": os.path.relpath(traffic_rec["_file"], ROOT)
-                   if "_file" in traffic_rec else f"profiles/traffic_{kernel}_{cfg.name}.json"}
+        # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, each scaled by
+        # what the same counter reads for a plain 1 GiB device copy
+        traffic = traffic_rec["fetch_bytes_per_launch"] + traffic_rec["write_bytes_per_launch"]
+        traffic_detail = {"fetch_bytes": traffic_rec["fetch_bytes_per_launch"],
+                          "write_bytes": traffic_rec["write_bytes_per_launch"],
+                          "fetch_scale": traffic_rec["fetch_scale"],
+                          "write_scale": traffic_rec["write_scale"],
+                          "source": f"profiles/traffic_{kernel}_{cfg.name}.json"}
     if path == "stream":
         achieved = gu_bytes / (gu_ms / 1e3) / 1e9
         roof = {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "algorithmic_bytes": gu_bytes, "avg_launch_ms": round(gu_ms, 5),
-                "traffic": traffic}
+                "traffic": traffic, "traffic_detail": traffic_detail}
         layer = {"hbm_frac": round(layer_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                  "algorithmic_bytes": layer_bytes}
     else:
@@ -222,7 +227,8 @@ def main():
         achieved = gu_flop / (gu_ms / 1e3) / 1e12
         roof = {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "algorithmic_flop": gu_flop,
-                "avg_launch_ms": round(gu_ms, 5), "traffic": traffic}
+                "avg_launch_ms": round(gu_ms, 5), "traffic": traffic,
+                "traffic_detail": traffic_detail}
         layer = {"mfma_frac": round(layer_flop / (ms_step / 1e3) / 1e12 / peak, 4),
                  "algorithmic_flop": layer_flop}
 
