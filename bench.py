@@ -46,6 +46,10 @@ def parse():
                     help="approximate budget of the CPU-oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "stream", "tiled"])
+    ap.add_argument("--sweep", default="",
+                    help="comma-separated batch sizes T: time moe_forward on both expert paths "
+                         "at each T with the workload's d, h and distributions (prints one JSON "
+                         "line with the table instead of the bench line)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (steps "
                          "times): the reference kernel for scaling HBM byte counters")
@@ -67,6 +71,59 @@ def copy_probe(mib: int, steps: int):
     print(json.dumps({"copy_probe_mib": mib, "read_bytes": n * 4, "write_bytes": n * 4,
                       "ms_per_copy": round(dt * 1e3, 4),
                       "GBps_read_plus_write": round(2 * n * 4 / dt / 1e9, 1)}), flush=True)
+    return 0
+
+
+def sweep(args):
+    """Tokens/s of the whole layer (one moe_forward call per step) against the batch
+    size, for the streaming and the tiled expert path and for the automatic choice."""
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import sparse_mixture_experts_wg_amd as moe
+    from tests import parity
+
+    Ts = sorted({int(t) for t in args.sweep.split(",") if t.strip()})
+    base = mi.CONFIGS[args.workload]
+    cfg = base.with_(name=f"{base.name}_sweep", T=max(Ts))
+    print(f"# sweep over T={Ts} with d={cfg.d} h={cfg.h} E={cfg.E} K={cfg.K} {cfg.dtype}",
+          file=sys.stderr, flush=True)
+    inp = mi.make_inputs(cfg, seed=0)
+    copies = max(1, args.weight_copies)
+    wsets = [{k: parity.device_array(inp[k], cfg.dtype) for k in ("w1", "w3", "w2")}
+             for _ in range(copies)]
+    w_g = parity.device_array(inp["w_g"], cfg.dtype)
+    rows = []
+    for T in Ts:
+        x = parity.device_array(np.ascontiguousarray(inp["x"][:T]), cfg.dtype)
+        y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+        row = {"T": T}
+        for path in ("stream", "tiled", "auto"):
+            p = moe.problem(T, cfg.d, cfg.h, cfg.E, cfg.K, cfg.dtype, "f32", path)
+            if path == "auto":
+                row["auto"] = "stream" if moe.resolve_path(p) == moe.PATH_STREAM else "tiled"
+                continue
+            wsb = torch.empty((moe.forward_workspace_bytes(p),), dtype=torch.uint8, device="cuda")
+            for i in range(3):
+                ws = wsets[i % copies]
+                moe.forward(p, x, w_g, ws["w1"], ws["w3"], ws["w2"], y, ws=wsb)
+            torch.cuda.synchronize()
+            n = max(5, min(args.steps, 40))
+            t0 = time.perf_counter()
+            for i in range(n):
+                ws = wsets[i % copies]
+                moe.forward(p, x, w_g, ws["w1"], ws["w3"], ws["w2"], y, ws=wsb)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / n
+            row[f"{path}_ms"] = round(ms, 4)
+            row[f"{path}_tokens_per_s"] = round(T / (ms / 1e3), 1)
+        row["best"] = "stream" if row["stream_ms"] <= row["tiled_ms"] else "tiled"
+        print(f"# T={T:5d} stream {row['stream_ms']:8.3f} ms  tiled {row['tiled_ms']:8.3f} ms  "
+              f"auto={row['auto']}", file=sys.stderr, flush=True)
+        rows.append(row)
+    print(json.dumps({"sweep": cfg.name, "d": cfg.d, "h": cfg.h, "E": cfg.E, "K": cfg.K,
+                      "dtype": cfg.dtype, "weight_copies": copies, "rows": rows}), flush=True)
     return 0
 
 
@@ -104,6 +161,8 @@ def main():
 
     if args.copy_probe_mib:
         return copy_probe(args.copy_probe_mib, max(1, args.steps))
+    if args.sweep:
+        return sweep(args)
 
     import numpy as np
     import torch
@@ -141,7 +200,7 @@ def main():
     o_perm = torch.empty((S, d), dtype=f32, device="cuda")
     y = torch.empty((T, d), dtype=f32, device="cuda")
 
-    def step(i, ev=None):
+    def step(i, ev=None, gu=None):
         ws = wsets[i % copies]
         if ev is not None:
             ev[0].record()
@@ -149,7 +208,11 @@ def main():
         moe.permute(p, dev["x"], idx, offsets, perm, slot, x_perm)
         if ev is not None:
             ev[1].record()
+        if gu is not None:
+            gu[0].record()
         moe.expert_gate_up(p, x_perm, offsets, ws["w1"], ws["w3"], act)
+        if gu is not None:
+            gu[1].record()
         if ev is not None:
             ev[2].record()
         moe.expert_down(p, act, offsets, ws["w2"], o_perm)
@@ -165,18 +228,31 @@ def main():
     torch.cuda.synchronize()
     counts = np.diff(parity.host_array(offsets).astype(np.int64))
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # Timed region: exactly `steps` steps. The only events inside it bracket the
+    # dominant kernel (gate-up) on the stream it is launched on (torch's current
+    # stream, which the binding passes to the library).
+    gu_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                 for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, events[i])
+        step(i, gu=gu_events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    gu_ms_live = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in gu_events]))
+    tokens_per_s = T / (ms_step / 1e3)
+
+    # Stage breakdown: a separate, shorter pass with events between all stages
+    # (events add a few microseconds each, so this pass is not the timed one).
+    n_diag = max(3, min(args.steps, 30))
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_diag)]
+    for i in range(n_diag):
+        step(i, events[i])
+    torch.cuda.synchronize()
     stage = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(4)] for ev in events])
     stage_ms = stage.mean(axis=0)
     gpu_ms_step = float(np.mean([ev[0].elapsed_time(ev[4]) for ev in events]))
-    tokens_per_s = T / (ms_step / 1e3)
 
     # one-call API on the same inputs, for comparison (not part of the timed region)
     ws_fwd = torch.empty((moe.forward_workspace_bytes(p),), dtype=torch.uint8, device="cuda")
@@ -195,7 +271,7 @@ def main():
     # ---- roofline of the dominant kernel (gate-up) --------------------------------
     es = 2 if cfg.dtype == "bf16" else 4
     hit = int(np.sum(counts > 0))
-    gu_ms = float(stage_ms[1])
+    gu_ms = gu_ms_live
     gu_bytes = hit * 2 * h * d * es + S * d * es + S * h * es
     gu_flop = 2.0 * S * d * 2 * h
     layer_bytes = hit * 3 * h * d * es + d * E * es + T * d * es + T * d * 4
@@ -292,6 +368,7 @@ def main():
                       "down": round(float(stage_ms[2]), 5),
                       "combine": round(float(stage_ms[3]), 5)},
         "gpu_ms_per_step_events": round(gpu_ms_step, 5),
+        "stages_note": f"separate pass of {n_diag} steps with events between the stages",
         "ms_per_step_one_call_api": round(ms_forward, 5),
         "rows_per_expert": counts.tolist(),
         "parity_spot_check": spot,

@@ -52,11 +52,15 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-/* Expert-projection variant. STREAM: weight streaming for small batches
- * (every expert receives at most 64 rows, guaranteed when T <= 64); TILED:
- * LDS-tiled matrix-core GEMM for large batches. AUTO picks STREAM when
- * T <= 64, else TILED. float32 problems always use one plain tiled kernel. */
+/* Expert-projection variant. STREAM: weight streaming for small batches (an
+ * expert's rows are taken 32 or 64 at a time, each group streaming the expert's
+ * weights; at most 2^21 routed rows); TILED: LDS-tiled matrix-core GEMM for
+ * large batches. AUTO picks STREAM when T <= MOE_STREAM_MAX_T, else TILED.
+ * float32 problems always use one plain tiled kernel. */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 } moe_path;
+
+/* Largest T for which MOE_PATH_AUTO picks MOE_PATH_STREAM. */
+#define MOE_STREAM_MAX_T 192
 
 typedef struct {
   int64_t T;         /* tokens                                   */
@@ -121,7 +125,6 @@ moe_status moe_permute(const moe_problem *p, const void *x, const int32_t *topk_
  *   offsets [E + 1]    int32, non-decreasing, offsets[0] = 0, offsets[E] <= S
  *   w1, w3  [E, h, d]  dtype
  *   act     [S, h]     dtype out (rows >= offsets[E] untouched)
- * The STREAM path requires offsets[e+1] - offsets[e] <= 64 for every e.
  */
 moe_status moe_expert_gate_up(const moe_problem *p, const void *x_perm, const int32_t *offsets,
                               const void *w1, const void *w3, void *act, void *stream);

@@ -30,10 +30,11 @@ moe_status ok() {
 
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
-constexpr int kStreamMaxT = 64;
 
 size_t esize(int dt) { return dt == MOE_BF16 ? 2 : 4; }
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int resolve(const moe_problem *p);
 
 moe_status check_problem(const moe_problem *p) {
   if (!p) return fail(MOE_ERR_NULL, "problem descriptor is NULL");
@@ -67,13 +68,17 @@ moe_status check_problem(const moe_problem *p) {
   const int64_t S = p->T * p->K;
   const int64_t tiles = (p->h / 128) * ((S + 255) / 256 + p->E);
   if (tiles > kMaxIndex / 2) return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch");
+  // stream grid: S / 32 row groups in the z dimension
+  if (p->dtype == MOE_BF16 && resolve(p) == MOE_PATH_STREAM && (S + 31) / 32 >= (int64_t(1) << 16))
+    return fail(MOE_ERR_UNSUPPORTED, "T=%lld too large for the STREAM path (use TILED)",
+                (long long)p->T);
   return MOE_OK;
 }
 
 int resolve(const moe_problem *p) {
   if (p->dtype == MOE_F32) return MOE_PATH_TILED;
   if (p->path != MOE_PATH_AUTO) return p->path;
-  return p->T <= kStreamMaxT ? MOE_PATH_STREAM : MOE_PATH_TILED;
+  return p->T <= MOE_STREAM_MAX_T ? MOE_PATH_STREAM : MOE_PATH_TILED;
 }
 
 moe_status check_ptr(const void *ptr, const char *name, bool required = true) {
@@ -150,7 +155,7 @@ moe_status do_gate_up(const moe_problem *p, const void *x_perm, const int32_t *o
                                 static_cast<float *>(act), p->E, S, int(p->d), int(p->h), s);
   else if (resolve(p) == MOE_PATH_STREAM)
     e = moe::launch_stream_gate_up(x_perm, offsets, w1, w3, act, p->E, int(p->d), int(p->h), p->T,
-                                   s);
+                                   S, s);
   else
     e = moe::launch_tiled_gate_up(x_perm, offsets, w1, w3, act, p->E, S, int(p->d), int(p->h), s);
   return hip_result(e, "gate-up launch");
@@ -165,7 +170,8 @@ moe_status do_down(const moe_problem *p, const void *act, const int32_t *offsets
                              static_cast<const float *>(w2), o_perm, p->E, S, int(p->d), int(p->h),
                              s);
   else if (resolve(p) == MOE_PATH_STREAM)
-    e = moe::launch_stream_down(act, offsets, w2, o_perm, p->E, int(p->d), int(p->h), p->T, s);
+    e = moe::launch_stream_down(act, offsets, w2, o_perm, p->E, int(p->d), int(p->h), p->T, S,
+                                s);
   else
     e = moe::launch_tiled_down(act, offsets, w2, o_perm, p->E, S, int(p->d), int(p->h), s);
   return hip_result(e, "down launch");

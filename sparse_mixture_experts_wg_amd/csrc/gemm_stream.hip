@@ -26,7 +26,8 @@
 //    registers with the stage they belong to; rows past the expert's end are
 //    clamped duplicates whose results are never stored. An expert with no rows
 //    exits before reading any weight; one with more rows than the accumulators
-//    hold is handled 16*KMT rows at a time (the weights stream once per group).
+//    hold is split into groups of 16*KMT rows run by separate workgroups (each
+//    group streams the expert's weights once more).
 //  * Gate-up carries W1 and W3 rows of the same output columns, so the SwiGLU
 //    epilogue silu(g) * u happens in registers before the single rounding to
 //    bf16 (notion page, "Implementation").
@@ -64,8 +65,8 @@ template <int NMAT, int NT, int MT, int PD>
 __device__ __forceinline__ void stream_rows(const uint16_t *__restrict__ X,
                                             const uint16_t *__restrict__ Wa,
                                             const uint16_t *__restrict__ Wb,
-                                            void *__restrict__ out, int N, int K, int e, int row0,
-                                            int ne, lds_char *lds) {
+                                            void *__restrict__ out, int N, int K, int e, int cb,
+                                            int row0, int ne, lds_char *lds) {
   constexpr int NTILE = NMAT * NT;  // 16-row weight tiles: tile t = m * NT + nt
   constexpr int NR = NTILE * 16;    // weight rows per stage
   constexpr int NI = NR / 8;        // DMA instructions per stage
@@ -76,7 +77,7 @@ __device__ __forceinline__ void stream_rows(const uint16_t *__restrict__ X,
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * (16 * NT);
+  const int n0 = cb * (16 * NT);
   const int nks = K >> 6;  // 64-wide k-stages (K is a multiple of 128)
   const int s0 = (wave * nks) / kSplitK, s1 = ((wave + 1) * nks) / kSplitK;
   lds_char *ring = lds + wave * (NS * SB);
@@ -221,6 +222,11 @@ __device__ __forceinline__ void stream_rows(const uint16_t *__restrict__ X,
     }
 }
 
+// Grid: (column blocks, E, row groups of 16*KMT rows). The row group is the
+// slowest index: workgroups that read the same weight rows at the same time
+// contend for the same lines (measured several times slower than one pass), so
+// an expert's later row groups run after every first group and re-read its
+// weights; workgroups of a row group an expert does not have exit at once.
 template <int NMAT, int NT, int KMT, int PD>
 __global__ __launch_bounds__(64 * kSplitK) void stream_kernel(const uint16_t *__restrict__ X,
                                                               const int32_t *__restrict__ offsets,
@@ -232,24 +238,23 @@ __global__ __launch_bounds__(64 * kSplitK) void stream_kernel(const uint16_t *__
   static_assert((kSplitK - 1) * NMAT * NT * KMT * 64 * 16 <= kLds, "reduction space");
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
   const int e = blockIdx.y;
+  const int cb = blockIdx.x;
+  const int rg = blockIdx.z * (16 * KMT);
   const int seg0 = offsets[e];
-  const int seg_rows = offsets[e + 1] - seg0;
-  // Rows are taken 16*KMT at a time; the accumulator count follows the rows of
-  // the group so that a 5-row expert does not pay for 4 token tiles.
-  for (int rg = 0; rg < seg_rows; rg += 16 * KMT) {
-    const int rows = min(seg_rows - rg, 16 * KMT);
-    const int mt = (rows + 15) >> 4;
-    lds_char *l = (lds_char *)lds;
-    if (mt == 1)
-      stream_rows<NMAT, NT, 1, PD>(X, Wa, Wb, out, N, K, e, seg0 + rg, rows, l);
-    else if (KMT >= 2 && mt == 2)
-      stream_rows<NMAT, NT, (KMT >= 2 ? 2 : 1), PD>(X, Wa, Wb, out, N, K, e, seg0 + rg, rows, l);
-    else if (KMT >= 3 && mt == 3)
-      stream_rows<NMAT, NT, (KMT >= 3 ? 3 : 1), PD>(X, Wa, Wb, out, N, K, e, seg0 + rg, rows, l);
-    else
-      stream_rows<NMAT, NT, KMT, PD>(X, Wa, Wb, out, N, K, e, seg0 + rg, rows, l);
-    __syncthreads();
-  }
+  const int rows = min(offsets[e + 1] - seg0 - rg, 16 * KMT);
+  if (rows <= 0) return;  // also every workgroup of an expert with no rows
+  // the accumulator count follows the rows of the group, so that a 5-row expert
+  // does not pay for 4 token tiles
+  const int mt = (rows + 15) >> 4;
+  lds_char *l = (lds_char *)lds;
+  if (mt == 1)
+    stream_rows<NMAT, NT, 1, PD>(X, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
+  else if (KMT >= 2 && mt == 2)
+    stream_rows<NMAT, NT, (KMT >= 2 ? 2 : 1), PD>(X, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
+  else if (KMT >= 3 && mt == 3)
+    stream_rows<NMAT, NT, (KMT >= 3 ? 3 : 1), PD>(X, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
+  else
+    stream_rows<NMAT, NT, KMT, PD>(X, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
 }
 
 // Measured on MI355X (decode, 8 experts of 14336 x 4096): gate-up with 2 x 32
@@ -260,38 +265,51 @@ constexpr int kNTDownSmall = 2, kNTDownLarge = 4, kPDDown = 2;
 
 }  // namespace
 
-// max_rows: an upper bound of the rows of any expert (T for a routed batch);
-// it only selects how many token tiles the accumulators hold.
+// rows_hint: the rows an expert usually has at most (T for a routed batch, whose
+// experts get one row per token at most); it selects how many token tiles the
+// accumulators hold. rows_bound: a bound no segment can exceed (S = offsets[E]
+// at most); it sets how many row groups the grid provides.
 hipError_t launch_stream_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
-                                 const void *w3, void *act, int E, int d, int h, int64_t max_rows,
-                                 hipStream_t s) {
-  const dim3 grid(unsigned(h / (16 * kNTGateUp)), unsigned(E));
+                                 const void *w3, void *act, int E, int d, int h, int64_t rows_hint,
+                                 int64_t rows_bound, hipStream_t s) {
   auto X = static_cast<const uint16_t *>(x_perm);
   auto A = static_cast<const uint16_t *>(w1);
   auto B = static_cast<const uint16_t *>(w3);
-  if (max_rows <= 32)
-    hipLaunchKernelGGL((stream_kernel<2, kNTGateUp, 2, kPDGateUp>), grid, dim3(64 * kSplitK), 0,
-                       s, X, offsets, A, B, act, h, d);
-  else
-    hipLaunchKernelGGL((stream_kernel<2, kNTGateUp, 4, kPDGateUp>), grid, dim3(64 * kSplitK), 0,
-                       s, X, offsets, A, B, act, h, d);
+  const int ncb = h / (16 * kNTGateUp);
+  if (rows_hint <= 32) {
+    const int nz = int((rows_bound + 31) / 32);
+    hipLaunchKernelGGL((stream_kernel<2, kNTGateUp, 2, kPDGateUp>),
+                       dim3(unsigned(ncb), unsigned(E), unsigned(nz)), dim3(64 * kSplitK), 0, s, X,
+                       offsets, A, B, act, h, d);
+  } else {
+    const int nz = int((rows_bound + 63) / 64);
+    hipLaunchKernelGGL((stream_kernel<2, kNTGateUp, 4, kPDGateUp>),
+                       dim3(unsigned(ncb), unsigned(E), unsigned(nz)), dim3(64 * kSplitK), 0, s, X,
+                       offsets, A, B, act, h, d);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_stream_down(const void *act, const int32_t *offsets, const void *w2,
-                              float *o_perm, int E, int d, int h, int64_t max_rows, hipStream_t s) {
+                              float *o_perm, int E, int d, int h, int64_t rows_hint,
+                              int64_t rows_bound, hipStream_t s) {
   auto X = static_cast<const uint16_t *>(act);
   auto A = static_cast<const uint16_t *>(w2);
   auto B = static_cast<const uint16_t *>(nullptr);
   auto O = static_cast<void *>(o_perm);
-  if (max_rows <= 32)
+  if (rows_hint <= 32) {
+    const int nz = int((rows_bound + 31) / 32);
+    const int ncb = d / (16 * kNTDownSmall);
     hipLaunchKernelGGL((stream_kernel<1, kNTDownSmall, 2, kPDDown>),
-                       dim3(unsigned(d / (16 * kNTDownSmall)), unsigned(E)), dim3(64 * kSplitK), 0,
-                       s, X, offsets, A, B, O, d, h);
-  else
+                       dim3(unsigned(ncb), unsigned(E), unsigned(nz)), dim3(64 * kSplitK), 0, s, X,
+                       offsets, A, B, O, d, h);
+  } else {
+    const int nz = int((rows_bound + 63) / 64);
+    const int ncb = d / (16 * kNTDownLarge);
     hipLaunchKernelGGL((stream_kernel<1, kNTDownLarge, 4, kPDDown>),
-                       dim3(unsigned(d / (16 * kNTDownLarge)), unsigned(E)), dim3(64 * kSplitK), 0,
-                       s, X, offsets, A, B, O, d, h);
+                       dim3(unsigned(ncb), unsigned(E), unsigned(nz)), dim3(64 * kSplitK), 0, s, X,
+                       offsets, A, B, O, d, h);
+  }
   return hipGetLastError();
 }
 

@@ -34,12 +34,16 @@ hipError_t launch_gather_rows(const void *x, const int32_t *perm_token, const in
                               int E, int64_t S, int64_t row_bytes, void *x_perm, hipStream_t s);
 
 // ---- expert projections -------------------------------------------------------
-// STREAM path (bf16; fast while every expert has <= 64 rows).
+// STREAM path (bf16 weight streaming; an expert's rows are taken in groups of 32
+// or 64, each group streaming its weights). rows_hint: usual largest segment
+// (T); rows_bound: no segment is longer (S); the grid's z extent is
+// rows_bound / 32 or / 64, which the caller keeps below 2^16.
 hipError_t launch_stream_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
-                                 const void *w3, void *act, int E, int d, int h, int64_t max_rows,
-                                 hipStream_t s);
+                                 const void *w3, void *act, int E, int d, int h, int64_t rows_hint,
+                                 int64_t rows_bound, hipStream_t s);
 hipError_t launch_stream_down(const void *act, const int32_t *offsets, const void *w2,
-                              float *o_perm, int E, int d, int h, int64_t max_rows, hipStream_t s);
+                              float *o_perm, int E, int d, int h, int64_t rows_hint,
+                              int64_t rows_bound, hipStream_t s);
 // TILED path (bf16 matrix cores).
 hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
                                 const void *w3, void *act, int E, int64_t S, int d, int h,

@@ -44,6 +44,8 @@ def test_status_strings():
     (dict(h=200), binding.ERR_UNSUPPORTED),
     (dict(dtype="f32", path="stream"), binding.ERR_UNSUPPORTED),
     (dict(T=1 << 31), binding.ERR_UNSUPPORTED),
+    # the streaming path takes at most 2^21 routed rows (row groups in the grid's z)
+    (dict(T=1 << 20, path="stream"), binding.ERR_UNSUPPORTED),
 ])
 def test_problem_validation(kw, code):
     p = _p(**kw)
@@ -67,8 +69,9 @@ def test_bad_dtype_and_reserved():
 
 
 def test_path_resolution():
-    assert moe.resolve_path(_p(T=64)) == binding.PATH_STREAM
-    assert moe.resolve_path(_p(T=65)) == binding.PATH_TILED
+    # the automatic switch point comes from a batch-size sweep on MI355X (bench.py --sweep)
+    assert moe.resolve_path(_p(T=192)) == binding.PATH_STREAM
+    assert moe.resolve_path(_p(T=193)) == binding.PATH_TILED
     assert moe.resolve_path(_p(T=4096, path="stream")) == binding.PATH_STREAM
     assert moe.resolve_path(_p(T=8, path="tiled")) == binding.PATH_TILED
     assert moe.resolve_path(_p(dtype="f32")) == binding.PATH_TILED

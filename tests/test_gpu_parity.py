@@ -58,7 +58,9 @@ SMALL = [
     # name, config, path
     ("tiny_f32", mi.CONFIGS["tiny_f32"], "auto"),
     ("bf16_tiled_ragged", mi.Config("s1", T=1000, d=256, h=640, wg_std="fan_in_d"), "tiled"),
-    ("bf16_tiled_T65", mi.Config("s2", T=65, d=384, h=256, wg_std="fan_in_d"), "auto"),
+    ("bf16_tiled_T65", mi.Config("s2", T=65, d=384, h=256, wg_std="fan_in_d"), "tiled"),
+    ("bf16_auto_T193_tiled", mi.Config("s2b", T=193, d=384, h=256, wg_std="fan_in_d"), "auto"),
+    ("bf16_auto_T192_stream", mi.Config("s2c", T=192, d=256, h=384, wg_std="fan_in_d"), "auto"),
     ("bf16_stream_T64", mi.Config("s3", T=64, d=512, h=1024, wg_std="fan_in_d"), "auto"),
     ("bf16_stream_T7", mi.Config("s4", T=7, d=256, h=384, wg_std="fan_in_d"), "stream"),
     ("bf16_stream_T100_multigroup", mi.Config("s5", T=100, d=256, h=256, wg_std="fan_in_d"),
@@ -261,6 +263,9 @@ EXPERT_CASES = [
     ("stream_mixed", "stream", 64, 512, 640, [0, 5, 64, 1, 0, 33, 17, 2]),
     ("stream_small", "stream", 32, 256, 384, [3, 0, 0, 16, 32, 1, 0, 4]),
     ("stream_over64", "stream", 150, 256, 256, [150, 0, 70, 0, 0, 0, 0, 1]),
+    # segments longer than T are allowed by the offsets contract (up to S = T*K)
+    ("stream_segment_over_T", "stream", 40, 256, 256, [70, 0, 0, 0, 0, 0, 0, 10]),
+    ("stream_T16_segment_30", "stream", 16, 256, 256, [30, 0, 2, 0, 0, 0, 0, 0]),
     ("tiled_mixed", "tiled", 1500, 256, 640, [0, 300, 1, 256, 513, 0, 77, 1000]),
     ("tiled_one", "tiled", 40, 128, 128, [0, 0, 0, 0, 0, 0, 0, 1]),
     ("tiled_d384", "tiled", 600, 384, 256, [200, 57, 0, 0, 300, 0, 1, 9]),
