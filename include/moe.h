@@ -26,7 +26,7 @@
  *    with a message from moe_last_error() (per thread). A device fault surfaces
  *    at the caller's next synchronisation.
  *  - Supported problems: 1 <= E <= 8, K in {1, 2}, K <= E, T >= 1,
- *    T*K < 2^31, d and h positive multiples of 128 up to 2^20, h*d < 2^31.
+ *    T <= 2^26, d and h positive multiples of 128 up to 2^20, h*d < 2^31.
  *  - Results are deterministic: no atomics take part in any value, and every
  *    sum has a fixed order.
  */

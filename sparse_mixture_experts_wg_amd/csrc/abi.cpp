@@ -53,7 +53,8 @@ moe_status check_problem(const moe_problem *p) {
   if (p->h * p->d > kMaxIndex)
     return fail(MOE_ERR_UNSUPPORTED, "h*d=%lld: one expert matrix must stay below 2^31 elements",
                 (long long)(p->h * p->d));
-  if (p->T > kMaxIndex / p->K || p->T > kMaxIndex / ((p->d + 1023) / 1024))
+  if (p->T > kMaxIndex / p->K || p->T > kMaxIndex / ((p->d + 1023) / 1024) ||
+      p->T > (int64_t(1) << 26))
     return fail(MOE_ERR_UNSUPPORTED, "T=%lld too large for 32-bit slot indices", (long long)p->T);
   if ((p->dtype != MOE_F32 && p->dtype != MOE_BF16) ||
       (p->out_dtype != MOE_F32 && p->out_dtype != MOE_BF16))

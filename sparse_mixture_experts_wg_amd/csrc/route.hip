@@ -5,13 +5,14 @@
 // x . W_gate of shape [tokens, 8]; keep the top 2 and renormalise with a
 // softmax) and notion page, sparse-gating equation G(x) = Softmax(TopK(x . W_g)).
 //
-// Layout of the work: a workgroup owns 8 tokens and its 4 wavefronts split the
-// dot products into quarters of d, so that even an 8-token batch keeps 4
-// wavefronts of loads in flight. A lane walks chunks of 8 consecutive rows j:
+// Layout of the work: a workgroup owns TPB tokens (1, 2 or 4 by batch size: a
+// small batch gets more workgroups, measured faster on MI355X) and its 4
+// wavefronts split the dot products into quarters of d, so that even a 1-token
+// batch keeps 4 wavefronts of loads in flight. A lane walks chunks of 8 consecutive rows j:
 // one 16-byte load of x per token (bf16) and the chunk's 8 rows of W_g (8 x 16
 // bytes for bf16 with E = 8; W_g is 64 KiB for d = 4096 and stays in L2),
-// reused by the 8 tokens; two chunks' loads are in flight before their FMAs.
-// Partial sums (8 tokens x 8 experts in float32) are finished by a butterfly
+// reused by the TPB tokens; two chunks' loads are in flight before their FMAs.
+// Partial sums (TPB tokens x 8 experts in float32) are finished by a butterfly
 // over the 64 lanes and a fixed-order sum of the 4 quarters in LDS. Logits stay
 // float32 up to the top-K decision.
 #include "kernels.h"
@@ -19,7 +20,6 @@
 namespace moe {
 namespace {
 
-constexpr int kTPB = 8;    // tokens per workgroup
 constexpr int kWaves = 4;  // wavefronts per workgroup, each a quarter of d
 
 // 8 consecutive elements as float.
@@ -63,7 +63,7 @@ __device__ __forceinline__ void load_wrow(const void *wg, int64_t j, int E, floa
   }
 }
 
-template <bool BF16, bool E8>
+template <bool BF16, bool E8, int kTPB>
 __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ x,
                                                     const void *__restrict__ wg, int64_t T, int d,
                                                     int E, int K, int32_t *__restrict__ idx,
@@ -154,22 +154,29 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ x,
 }
 
 template <bool BF16, bool E8>
-void launch(dim3 grid, hipStream_t s, const void *x, const void *wg, int64_t T, int d, int E, int K,
+void launch(hipStream_t s, const void *x, const void *wg, int64_t T, int d, int E, int K,
             int32_t *idx, float *w, float *logits) {
-  hipLaunchKernelGGL((route_kernel<BF16, E8>), grid, dim3(256), 0, s, x, wg, T, d, E, K, idx, w,
-                     logits);
+  // tokens per workgroup by batch size (a sweep of T = 1 .. 16384 on MI355X)
+  if (T <= 256)
+    hipLaunchKernelGGL((route_kernel<BF16, E8, 1>), dim3(unsigned(T)), dim3(256), 0, s, x, wg, T,
+                       d, E, K, idx, w, logits);
+  else if (T <= 1024)
+    hipLaunchKernelGGL((route_kernel<BF16, E8, 2>), dim3(unsigned((T + 1) / 2)), dim3(256), 0, s,
+                       x, wg, T, d, E, K, idx, w, logits);
+  else
+    hipLaunchKernelGGL((route_kernel<BF16, E8, 4>), dim3(unsigned((T + 3) / 4)), dim3(256), 0, s,
+                       x, wg, T, d, E, K, idx, w, logits);
 }
 
 }  // namespace
 
 hipError_t launch_route(bool bf16, const void *x, const void *wg, int64_t T, int d, int E, int K,
                         int32_t *idx, float *w, float *logits, hipStream_t s) {
-  const dim3 grid(unsigned((T + kTPB - 1) / kTPB));
   const bool e8 = (E == 8);
-  if (bf16 && e8) launch<true, true>(grid, s, x, wg, T, d, E, K, idx, w, logits);
-  else if (bf16) launch<true, false>(grid, s, x, wg, T, d, E, K, idx, w, logits);
-  else if (e8) launch<false, true>(grid, s, x, wg, T, d, E, K, idx, w, logits);
-  else launch<false, false>(grid, s, x, wg, T, d, E, K, idx, w, logits);
+  if (bf16 && e8) launch<true, true>(s, x, wg, T, d, E, K, idx, w, logits);
+  else if (bf16) launch<true, false>(s, x, wg, T, d, E, K, idx, w, logits);
+  else if (e8) launch<false, true>(s, x, wg, T, d, E, K, idx, w, logits);
+  else launch<false, false>(s, x, wg, T, d, E, K, idx, w, logits);
   return hipGetLastError();
 }
 
