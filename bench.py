@@ -184,8 +184,11 @@ def main():
     wsets = []
     for c in range(copies):
         wsets.append({k: parity.device_array(inp[k], cfg.dtype) for k in ("w1", "w3", "w2")})
-    p = moe.problem(T, d, h, E, K, cfg.dtype, "f32", args.path)
+    # the staged calls let the down projection leave partial sums for the combine, as
+    # the one-call entry point does internally
+    p = moe.problem(T, d, h, E, K, cfg.dtype, "f32", args.path, moe.FLAG_DOWN_PARTIALS)
     path = "stream" if moe.resolve_path(p) == moe.PATH_STREAM else "tiled"
+    parts = moe.down_parts(p)
     if cfg.dtype == "f32":
         path = "f32"
     f32 = torch.float32
@@ -197,7 +200,7 @@ def main():
     slot = torch.empty((T, K), dtype=torch.int32, device="cuda")
     x_perm = torch.empty((S, d), dtype=dt, device="cuda")
     act = torch.empty((S, h), dtype=dt, device="cuda")
-    o_perm = torch.empty((S, d), dtype=f32, device="cuda")
+    o_perm = torch.empty((S, d) if parts == 1 else (parts, S, d), dtype=f32, device="cuda")
     y = torch.empty((T, d), dtype=f32, device="cuda")
 
     def step(i, ev=None, gu=None):
@@ -359,7 +362,7 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded generator; random-init weights of the layer's shape)",
         "config": {"workload": cfg.name, "T": T, "d": d, "h": h, "E": E, "K": K,
-                   "path": path, "weight_copies": copies},
+                   "path": path, "down_partial_sums": parts, "weight_copies": copies},
         "roofline": roof,
         "layer": layer,
         "cpu_baseline": cpu,

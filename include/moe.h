@@ -62,6 +62,14 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 } moe_
 /* Largest T for which MOE_PATH_AUTO picks MOE_PATH_STREAM. */
 #define MOE_STREAM_MAX_T 192
 
+/* moe_problem.flags bits.
+ * MOE_FLAG_DOWN_PARTIALS: the caller lets moe_expert_down / moe_expert_swiglu
+ *   split the sum over h into moe_down_parts(p) float32 partial sums, stored one
+ *   after another in o_perm ([parts, S, d]), and moe_combine (given the same
+ *   flags) adds them in part order before weighting. With few row tiles per
+ *   expert this keeps every compute unit busy in the down projection. */
+#define MOE_FLAG_DOWN_PARTIALS 1
+
 typedef struct {
   int64_t T;         /* tokens                                   */
   int64_t d;         /* model dimension                          */
@@ -71,7 +79,7 @@ typedef struct {
   int32_t dtype;     /* moe_dtype of x, W_g, W1, W3, W2, act     */
   int32_t out_dtype; /* moe_dtype of y                           */
   int32_t path;      /* moe_path                                 */
-  int32_t reserved;  /* must be 0                                */
+  int32_t flags;     /* MOE_FLAG_* bits, 0 for none              */
 } moe_problem;
 
 /* Human-readable name of a status code. */
@@ -79,6 +87,12 @@ const char *moe_status_string(int status);
 
 /* Detail of the last error returned on this thread ("" if none). */
 const char *moe_last_error(void);
+
+/* Number of float32 partial sums per row that moe_expert_down and
+ * moe_expert_swiglu write into o_perm for `p` (1, or 2 when p->flags has
+ * MOE_FLAG_DOWN_PARTIALS and the down projection is split), or -status if `p`
+ * is invalid. o_perm then holds parts * S * d floats. */
+int moe_down_parts(const moe_problem *p);
 
 /* Which expert-projection variant `p` runs on (MOE_PATH_STREAM or
  * MOE_PATH_TILED), or a negative moe_status if `p` is invalid. Host only. */
@@ -135,7 +149,9 @@ moe_status moe_expert_gate_up(const moe_problem *p, const void *x_perm, const in
  *   act     [S, h]     dtype
  *   offsets [E + 1]    int32 (as above)
  *   w2      [E, d, h]  dtype
- *   o_perm  [S, d]     float32 out (rows >= offsets[E] untouched)
+ *   o_perm  [S, d]     float32 out (rows >= offsets[E] untouched); with
+ *                      MOE_FLAG_DOWN_PARTIALS [parts, S, d] partial sums,
+ *                      parts = moe_down_parts(p)
  */
 moe_status moe_expert_down(const moe_problem *p, const void *act, const int32_t *offsets,
                            const void *w2, float *o_perm, void *stream);
@@ -145,7 +161,8 @@ size_t moe_expert_workspace_bytes(const moe_problem *p);
 
 /*
  * Both expert projections: o_perm[r] = SwiGLU_e(x_perm[r]) for every segment,
- * with the hidden activations in `ws` (at least moe_expert_workspace_bytes).
+ * with the hidden activations in `ws` (at least moe_expert_workspace_bytes);
+ * o_perm as for moe_expert_down.
  */
 moe_status moe_expert_swiglu(const moe_problem *p, const void *x_perm, const int32_t *offsets,
                              const void *w1, const void *w3, const void *w2, float *o_perm,
@@ -156,8 +173,9 @@ moe_status moe_expert_swiglu(const moe_problem *p, const void *x_perm, const int
  * float32 in k order, rounded once to out_dtype (crackai page,
  * y = w_1 Expert_i1(x) + w_2 Expert_i2(x); notion page, output equation).
  * Slots with slot_pos outside [0, T*K) (-1 marks a dropped slot) contribute
- * nothing.
- *   o_perm   [S, d]  float32
+ * nothing. With MOE_FLAG_DOWN_PARTIALS, o_perm[r] is the sum of the
+ * moe_down_parts(p) partials of row r, added in part order.
+ *   o_perm   [S, d]  float32 ([parts, S, d] with MOE_FLAG_DOWN_PARTIALS)
  *   slot_pos [T, K]  int32
  *   topk_w   [T, K]  float32
  *   y        [T, d]  out_dtype out

@@ -7,13 +7,15 @@ kernels in libmoe.so behind the C ABI of include/moe.h; this package is the
 Python binding (torch tensors in, torch tensors out).
 """
 from .binding import (  # noqa: F401
-    BF16, F32, PATH_AUTO, PATH_STREAM, PATH_TILED, MoeError, Problem, combine, expert_down,
-    expert_gate_up, expert_swiglu, expert_workspace_bytes, forward, forward_workspace_bytes,
-    header_functions, last_error, lib, permute, problem, resolve_path, route, status_string,
+    BF16, F32, FLAG_DOWN_PARTIALS, PATH_AUTO, PATH_STREAM, PATH_TILED, MoeError, Problem,
+    combine, down_parts, expert_down, expert_gate_up, expert_swiglu, expert_workspace_bytes,
+    forward, forward_workspace_bytes, header_functions, last_error, lib, permute, problem,
+    resolve_path, route, status_string,
 )
 
 __all__ = [
     "Problem", "problem", "route", "permute", "expert_gate_up", "expert_down", "expert_swiglu",
     "combine", "forward", "expert_workspace_bytes", "forward_workspace_bytes", "resolve_path",
+    "down_parts",
     "MoeError", "status_string", "last_error", "header_functions",
 ]

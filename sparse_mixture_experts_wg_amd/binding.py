@@ -21,6 +21,7 @@ F32, BF16 = 0, 1
 PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 2
 _DTYPES = {"f32": F32, "bf16": BF16}
 _PATHS = {"auto": PATH_AUTO, "stream": PATH_STREAM, "tiled": PATH_TILED}
+FLAG_DOWN_PARTIALS = 1
 
 
 class MoeError(RuntimeError):
@@ -33,7 +34,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("h", ctypes.c_int64),
                 ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32)]
 
     @property
     def S(self) -> int:
@@ -41,8 +42,8 @@ class Problem(ctypes.Structure):
 
 
 def problem(T: int, d: int, h: int, E: int = 8, K: int = 2, dtype: str = "bf16",
-            out_dtype: str = "f32", path: str = "auto") -> Problem:
-    return Problem(T, d, h, E, K, _DTYPES[dtype], _DTYPES[out_dtype], _PATHS[path], 0)
+            out_dtype: str = "f32", path: str = "auto", flags: int = 0) -> Problem:
+    return Problem(T, d, h, E, K, _DTYPES[dtype], _DTYPES[out_dtype], _PATHS[path], flags)
 
 
 def header_functions(path: str = HEADER):
@@ -68,6 +69,7 @@ def _load() -> ctypes.CDLL:
         "moe_status_string": ([i32], ctypes.c_char_p),
         "moe_last_error": ([], ctypes.c_char_p),
         "moe_resolve_path": ([P], i32),
+        "moe_down_parts": ([P], i32),
         "moe_route": ([P, vp, vp, vp, vp, vp, vp], i32),
         "moe_permute": ([P, vp, vp, vp, vp, vp, vp, vp], i32),
         "moe_expert_gate_up": ([P, vp, vp, vp, vp, vp, vp], i32),
@@ -107,6 +109,19 @@ def resolve_path(p: Problem) -> int:
 
 def expert_workspace_bytes(p: Problem) -> int:
     return lib.moe_expert_workspace_bytes(ctypes.byref(p))
+
+
+def down_parts(p: Problem) -> int:
+    """Partial sums per row that the down projection writes into o_perm for `p`."""
+    n = lib.moe_down_parts(ctypes.byref(p))
+    if n < 0:
+        raise MoeError(-n, last_error())
+    return n
+
+
+def _o_shape(p: Problem):
+    parts = down_parts(p)
+    return (p.S, int(p.d)) if parts == 1 else (parts, p.S, int(p.d))
 
 
 def forward_workspace_bytes(p: Problem) -> int:
@@ -203,11 +218,12 @@ def expert_down(p: Problem, act, offsets, w2, o_perm=None, stream=None):
     torch = _torch()
     d, h, E, S = int(p.d), int(p.h), int(p.E), p.S
     dt = _tdtype(p.dtype)
-    o_perm = _empty((S, d), torch.float32, act) if o_perm is None else o_perm
+    o_shape = _o_shape(p)
+    o_perm = _empty(o_shape, torch.float32, act) if o_perm is None else o_perm
     _check(lib.moe_expert_down(ctypes.byref(p), _ptr(act, "act", (S, h), dt),
                                _ptr(offsets, "offsets", (E + 1,), torch.int32),
                                _ptr(w2, "w2", (E, d, h), dt),
-                               _ptr(o_perm, "o_perm", (S, d), torch.float32), _stream(stream)))
+                               _ptr(o_perm, "o_perm", o_shape, torch.float32), _stream(stream)))
     return o_perm
 
 
@@ -215,14 +231,15 @@ def expert_swiglu(p: Problem, x_perm, offsets, w1, w3, w2, o_perm=None, ws=None,
     torch = _torch()
     d, h, E, S = int(p.d), int(p.h), int(p.E), p.S
     dt = _tdtype(p.dtype)
-    o_perm = _empty((S, d), torch.float32, x_perm) if o_perm is None else o_perm
+    o_shape = _o_shape(p)
+    o_perm = _empty(o_shape, torch.float32, x_perm) if o_perm is None else o_perm
     need = expert_workspace_bytes(p)
     ws = _empty((max(need, 1),), torch.uint8, x_perm) if ws is None else ws
     _check(lib.moe_expert_swiglu(ctypes.byref(p), _ptr(x_perm, "x_perm", (S, d), dt),
                                  _ptr(offsets, "offsets", (E + 1,), torch.int32),
                                  _ptr(w1, "w1", (E, h, d), dt), _ptr(w3, "w3", (E, h, d), dt),
                                  _ptr(w2, "w2", (E, d, h), dt),
-                                 _ptr(o_perm, "o_perm", (S, d), torch.float32), _ptr(ws, "ws"),
+                                 _ptr(o_perm, "o_perm", o_shape, torch.float32), _ptr(ws, "ws"),
                                  ws.numel() * ws.element_size(), _stream(stream)))
     return o_perm
 
@@ -232,7 +249,7 @@ def combine(p: Problem, o_perm, slot_pos, topk_w, y=None, stream=None):
     T, d, K, S = int(p.T), int(p.d), int(p.K), p.S
     yd = _tdtype(p.out_dtype)
     y = _empty((T, d), yd, o_perm) if y is None else y
-    _check(lib.moe_combine(ctypes.byref(p), _ptr(o_perm, "o_perm", (S, d), torch.float32),
+    _check(lib.moe_combine(ctypes.byref(p), _ptr(o_perm, "o_perm", _o_shape(p), torch.float32),
                            _ptr(slot_pos, "slot_pos", (T, K), torch.int32),
                            _ptr(topk_w, "topk_w", (T, K), torch.float32),
                            _ptr(y, "y", (T, d), yd), _stream(stream)))

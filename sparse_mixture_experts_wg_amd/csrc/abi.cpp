@@ -64,7 +64,8 @@ moe_status check_problem(const moe_problem *p) {
     return fail(MOE_ERR_UNSUPPORTED, "path=%d unknown", p->path);
   if (p->dtype == MOE_F32 && p->path == MOE_PATH_STREAM)
     return fail(MOE_ERR_UNSUPPORTED, "the STREAM path is bf16 only");
-  if (p->reserved != 0) return fail(MOE_ERR_UNSUPPORTED, "reserved field must be 0");
+  if (p->flags & ~MOE_FLAG_DOWN_PARTIALS)
+    return fail(MOE_ERR_UNSUPPORTED, "flags=0x%x: unknown bits", unsigned(p->flags));
   // tiled grid: column blocks x (token blocks + E) must fit a 1-D grid
   const int64_t S = p->T * p->K;
   const int64_t tiles = (p->h / 128) * ((S + 255) / 256 + p->E);
@@ -100,8 +101,23 @@ moe_status hip_result(hipError_t e, const char *what) {
   return MOE_OK;
 }
 
+// Partial sums of the down projection (see MOE_FLAG_DOWN_PARTIALS): the tiled
+// kernel splits the h sum in two when the row tiles of the down projection would
+// fill the 256 compute units fewer than 4 times over (with one tile per compute
+// unit at a time, the last, partly filled round then costs less).
+constexpr int64_t kCUs = 256;
+
+int down_parts(const moe_problem *p) {
+  if (!(p->flags & MOE_FLAG_DOWN_PARTIALS) || p->dtype != MOE_BF16) return 1;
+  if (resolve(p) != MOE_PATH_TILED || p->h % 256) return 1;
+  const int64_t S = p->T * p->K;
+  const int64_t tiles = (p->d / 256 + (p->d % 256 != 0)) * ((S + 255) / 256 + p->E);
+  return tiles < 4 * kCUs ? 2 : 1;
+}
+
 struct ForwardLayout {
   size_t idx, w, offsets, perm, slot, x_perm, act, o_perm, total;
+  int parts;
 };
 
 ForwardLayout forward_layout(const moe_problem *p) {
@@ -120,7 +136,10 @@ ForwardLayout forward_layout(const moe_problem *p) {
   L.slot = take(S * 4);
   L.x_perm = take(S * p->d * esize(p->dtype));
   L.act = take(S * p->h * esize(p->dtype));
-  L.o_perm = take(S * p->d * 4);
+  moe_problem q = *p;
+  q.flags |= MOE_FLAG_DOWN_PARTIALS;  // the layer's own o_perm may hold partials
+  L.parts = down_parts(&q);
+  L.o_perm = take(size_t(L.parts) * S * p->d * 4);
   L.total = at;
   return L;
 }
@@ -163,7 +182,7 @@ moe_status do_gate_up(const moe_problem *p, const void *x_perm, const int32_t *o
 }
 
 moe_status do_down(const moe_problem *p, const void *act, const int32_t *offsets, const void *w2,
-                   float *o_perm, hipStream_t s) {
+                   float *o_perm, int parts, hipStream_t s) {
   const int64_t S = p->T * p->K;
   hipError_t e;
   if (p->dtype == MOE_F32)
@@ -174,13 +193,13 @@ moe_status do_down(const moe_problem *p, const void *act, const int32_t *offsets
     e = moe::launch_stream_down(act, offsets, w2, o_perm, p->E, int(p->d), int(p->h), p->T, S,
                                 s);
   else
-    e = moe::launch_tiled_down(act, offsets, w2, o_perm, p->E, S, int(p->d), int(p->h), s);
+    e = moe::launch_tiled_down(act, offsets, w2, o_perm, p->E, S, int(p->d), int(p->h), parts, s);
   return hip_result(e, "down launch");
 }
 
-moe_status do_combine(const moe_problem *p, const float *o_perm, const int32_t *slot,
+moe_status do_combine(const moe_problem *p, const float *o_perm, int parts, const int32_t *slot,
                       const float *w, void *y, hipStream_t s) {
-  return hip_result(moe::launch_combine(o_perm, slot, w, p->T, p->K, int(p->d),
+  return hip_result(moe::launch_combine(o_perm, parts, slot, w, p->T, p->K, int(p->d),
                                         p->out_dtype == MOE_BF16, y, s),
                     "combine launch");
 }
@@ -214,6 +233,12 @@ const char *moe_status_string(int status) {
 }
 
 const char *moe_last_error(void) { return g_err; }
+
+int moe_down_parts(const moe_problem *p) {
+  const moe_status st = check_problem(p);
+  if (st != MOE_OK) return -int(st);
+  return down_parts(p);
+}
 
 int moe_resolve_path(const moe_problem *p) {
   const moe_status st = check_problem(p);
@@ -273,7 +298,7 @@ moe_status moe_expert_down(const moe_problem *p, const void *act, const int32_t 
     CHECK(check_ptr(offsets, "offsets"));
     CHECK(check_ptr(w2, "w2"));
     CHECK(check_ptr(o_perm, "o_perm"));
-    CHECK(do_down(p, act, offsets, w2, o_perm, as_stream(stream)));
+    CHECK(do_down(p, act, offsets, w2, o_perm, down_parts(p), as_stream(stream)));
     return ok();
   });
 }
@@ -300,7 +325,7 @@ moe_status moe_expert_swiglu(const moe_problem *p, const void *x_perm, const int
       return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
     const hipStream_t s = as_stream(stream);
     CHECK(do_gate_up(p, x_perm, offsets, w1, w3, ws, s));
-    CHECK(do_down(p, ws, offsets, w2, o_perm, s));
+    CHECK(do_down(p, ws, offsets, w2, o_perm, down_parts(p), s));
     return ok();
   });
 }
@@ -313,7 +338,7 @@ moe_status moe_combine(const moe_problem *p, const float *o_perm, const int32_t 
     CHECK(check_ptr(slot_pos, "slot_pos"));
     CHECK(check_ptr(topk_w, "topk_w"));
     CHECK(check_ptr(y, "y"));
-    CHECK(do_combine(p, o_perm, slot_pos, topk_w, y, as_stream(stream)));
+    CHECK(do_combine(p, o_perm, down_parts(p), slot_pos, topk_w, y, as_stream(stream)));
     return ok();
   });
 }
@@ -355,8 +380,8 @@ moe_status moe_forward(const moe_problem *p, const void *x, const void *w_g, con
     CHECK(do_route(p, x, w_g, idx, w, nullptr, s));
     CHECK(do_permute(p, x, idx, offsets, perm, slot, x_perm, s));
     CHECK(do_gate_up(p, x_perm, offsets, w1, w3, act, s));
-    CHECK(do_down(p, act, offsets, w2, o_perm, s));
-    CHECK(do_combine(p, o_perm, slot, w, y, s));
+    CHECK(do_down(p, act, offsets, w2, o_perm, L.parts, s));
+    CHECK(do_combine(p, o_perm, L.parts, slot, w, y, s));
     return ok();
   });
 }

@@ -4,14 +4,16 @@
 // + w_2 Expert_i2(x); notion page, output equation). Each token gathers its K
 // expert rows, so no two threads write the same output and no atomics are
 // needed; the K terms are added in k order with fused multiply-adds in float32
-// and the sum is rounded once to the output type.
+// and the sum is rounded once to the output type. When the down projection
+// left `parts` partial sums per row (parts * S * d floats), a row is their sum
+// in part order.
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o_perm,
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o_perm, int parts,
                                                       const int32_t *__restrict__ slot_pos,
                                                       const float *__restrict__ w, int64_t T,
                                                       int64_t S, int K, int d, int chunks,
@@ -24,7 +26,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     const int32_t p = slot_pos[t * K + k];
     if (p < 0 || p >= S) continue;
     const float wk = w[t * K + k];
-    const float4 o = *reinterpret_cast<const float4 *>(o_perm + int64_t(p) * d + col);
+    float4 o = *reinterpret_cast<const float4 *>(o_perm + int64_t(p) * d + col);
+    for (int q = 1; q < parts; ++q) {
+      const float4 oq =
+          *reinterpret_cast<const float4 *>(o_perm + (q * S + int64_t(p)) * d + col);
+      o.x += oq.x;
+      o.y += oq.y;
+      o.z += oq.z;
+      o.w += oq.w;
+    }
     acc.x = fmaf(wk, o.x, acc.x);
     acc.y = fmaf(wk, o.y, acc.y);
     acc.z = fmaf(wk, o.z, acc.z);
@@ -42,16 +52,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const float *o_perm, const int32_t *slot_pos, const float *w, int64_t T,
-                          int K, int d, bool out_bf16, void *y, hipStream_t s) {
+hipError_t launch_combine(const float *o_perm, int parts, const int32_t *slot_pos, const float *w,
+                          int64_t T, int K, int d, bool out_bf16, void *y, hipStream_t s) {
   const int chunks = (d + 1023) / 1024;
   const dim3 grid(unsigned(T * chunks));
   if (out_bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, o_perm, slot_pos, w, T, T * K, K,
-                       d, chunks, y);
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, o_perm, parts, slot_pos, w, T,
+                       T * K, K, d, chunks, y);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, o_perm, slot_pos, w, T, T * K, K,
-                       d, chunks, y);
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, o_perm, parts, slot_pos, w, T,
+                       T * K, K, d, chunks, y);
   return hipGetLastError();
 }
 

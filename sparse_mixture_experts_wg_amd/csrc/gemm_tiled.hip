@@ -30,6 +30,9 @@
 //    round-robin) owns one contiguous range of tiles and its own L2 sees the
 //    reuse. Token rows past an expert's end are clamped duplicates whose results
 //    are never stored.
+//  * Down with few row tiles can split the sum over h in two: each half is a
+//    tile of its own writing float32 partial sums that the combine step adds
+//    in a fixed order, so that the last round of tiles fills the GPU.
 #include "kernels.h"
 
 namespace moe {
@@ -49,17 +52,22 @@ __global__ __launch_bounds__(512) void tiled_kernel(const uint16_t *__restrict__
                                                      const int32_t *__restrict__ offsets, int E,
                                                      const uint16_t *__restrict__ Wa,
                                                      const uint16_t *__restrict__ Wb,
-                                                     void *__restrict__ out, int N, int K) {
+                                                     void *__restrict__ out, int N, int K,
+                                                     int ksplit, int64_t part_stride) {
   constexpr int BT = 256;
   constexpr int kCols = GATEUP ? 128 : 256;
   const int ct = (N + kCols - 1) / kCols;
   int total = 0;
   for (int q = 0; q < E; ++q) total += ct * ((offsets[q + 1] - offsets[q] + BT - 1) / BT);
-  const int g8 = (total + kXCD - 1) / kXCD;
+  // ksplit > 1 (down only): the sum over K is cut into ksplit ranges, part ks
+  // writing its float32 partial sums to out + ks * part_stride
+  const int g8 = (total * ksplit + kXCD - 1) / kXCD;
   const int b = blockIdx.x;
   if (b >= g8 * kXCD) return;
   int L = (b % kXCD) * g8 + b / kXCD;
-  if (L >= total) return;
+  if (L >= total * ksplit) return;
+  const int ks = L / total;
+  L -= ks * total;
   int e = 0, row0 = 0, ne = 0, mtiles = 0;
   for (; e < E; ++e) {
     row0 = offsets[e];
@@ -119,11 +127,12 @@ __global__ __launch_bounds__(512) void tiled_kernel(const uint16_t *__restrict__
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[f][t][i] = 0.f;
 
-  const int nk = K / 64;
+  const int nk = K / 64 / ksplit;  // k-blocks of this part (an even count)
+  const int kb0 = ks * nk;
 
 #define DMA(SW, SX, KB)                                                                    \
   {                                                                                        \
-    const uint32_t k0 = uint32_t(min(KB, nk - 1) * 64);                                    \
+    const uint32_t k0 = uint32_t((kb0 + min(KB, nk - 1)) * 64);                            \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                        \
       __builtin_amdgcn_global_load_lds(wmat + wofs[i] + k0,                                \
                                        (lds_void *)(SW + (dma_row + i * 8) * 64), 16, 0, 0); \
@@ -182,7 +191,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(const uint16_t *__restrict__
   for (int t = 0; t < 2; ++t) {
     const int tok = m0 + wc * 64 + t * 32 + (lane & 31);
     if (tok >= ne) continue;
-    const size_t orow = size_t(row0 + tok) * N;
+    const size_t orow = size_t(row0 + tok) * N + size_t(ks) * size_t(part_stride);
     if constexpr (GATEUP) {
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
@@ -216,9 +225,9 @@ __global__ __launch_bounds__(512) void tiled_kernel(const uint16_t *__restrict__
 }
 
 // Upper bound of the tile count for any split of S rows over E experts.
-inline unsigned tiled_grid(int64_t S, int E, int N, int cols) {
+inline unsigned tiled_grid(int64_t S, int E, int N, int cols, int ksplit) {
   const int64_t ct = (N + cols - 1) / cols;
-  const int64_t tiles = ct * ((S + 255) / 256 + E);
+  const int64_t tiles = ksplit * ct * ((S + 255) / 256 + E);
   return unsigned((tiles + kXCD - 1) / kXCD * kXCD);
 }
 
@@ -227,18 +236,20 @@ inline unsigned tiled_grid(int64_t S, int E, int N, int cols) {
 hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
                                  const void *w3, void *act, int E, int64_t S, int d, int h,
                                  hipStream_t s) {
-  hipLaunchKernelGGL((tiled_kernel<true>), dim3(tiled_grid(S, E, h, 128)), dim3(512), 0, s,
+  hipLaunchKernelGGL((tiled_kernel<true>), dim3(tiled_grid(S, E, h, 128, 1)), dim3(512), 0, s,
                      static_cast<const uint16_t *>(x_perm), offsets, E,
-                     static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3), act, h, d);
+                     static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3), act, h, d,
+                     1, int64_t(0));
   return hipGetLastError();
 }
 
 hipError_t launch_tiled_down(const void *act, const int32_t *offsets, const void *w2,
-                              float *o_perm, int E, int64_t S, int d, int h, hipStream_t s) {
-  hipLaunchKernelGGL((tiled_kernel<false>), dim3(tiled_grid(S, E, d, 256)), dim3(512), 0, s,
+                              float *o_perm, int E, int64_t S, int d, int h, int parts,
+                              hipStream_t s) {
+  hipLaunchKernelGGL((tiled_kernel<false>), dim3(tiled_grid(S, E, d, 256, parts)), dim3(512), 0, s,
                      static_cast<const uint16_t *>(act), offsets, E,
                      static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(nullptr),
-                     static_cast<void *>(o_perm), d, h);
+                     static_cast<void *>(o_perm), d, h, parts, S * d);
   return hipGetLastError();
 }
 

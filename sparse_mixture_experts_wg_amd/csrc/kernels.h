@@ -48,8 +48,11 @@ hipError_t launch_stream_down(const void *act, const int32_t *offsets, const voi
 hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
                                 const void *w3, void *act, int E, int64_t S, int d, int h,
                                 hipStream_t s);
+// parts (1 or 2; 2 needs h % 256 == 0): partial sums over h, part q at
+// o_perm + q * S * d.
 hipError_t launch_tiled_down(const void *act, const int32_t *offsets, const void *w2,
-                             float *o_perm, int E, int64_t S, int d, int h, hipStream_t s);
+                             float *o_perm, int E, int64_t S, int d, int h, int parts,
+                             hipStream_t s);
 // float32 problems.
 hipError_t launch_f32_gate_up(const float *x_perm, const int32_t *offsets, const float *w1,
                               const float *w3, float *act, int E, int64_t S, int d, int h,
@@ -58,7 +61,7 @@ hipError_t launch_f32_down(const float *act, const int32_t *offsets, const float
                            float *o_perm, int E, int64_t S, int d, int h, hipStream_t s);
 
 // ---- combine ----------------------------------------------------------------
-hipError_t launch_combine(const float *o_perm, const int32_t *slot_pos, const float *w, int64_t T,
-                          int K, int d, bool out_bf16, void *y, hipStream_t s);
+hipError_t launch_combine(const float *o_perm, int parts, const int32_t *slot_pos, const float *w,
+                          int64_t T, int K, int d, bool out_bf16, void *y, hipStream_t s);
 
 }  // namespace moe

@@ -56,13 +56,16 @@ def test_problem_validation(kw, code):
     assert moe.last_error()
 
 
-def test_bad_dtype_and_reserved():
+def test_bad_dtype_and_flags():
     p = _p()
     p.dtype = 7
     assert moe.resolve_path(p) == -binding.ERR_UNSUPPORTED
     p = _p()
-    p.reserved = 1
+    p.flags = 2  # unknown bit
     assert moe.resolve_path(p) == -binding.ERR_UNSUPPORTED
+    p = _p()
+    p.flags = binding.FLAG_DOWN_PARTIALS  # a known bit is accepted
+    assert moe.resolve_path(p) == binding.PATH_STREAM
     p = _p()
     p.path = 5
     assert moe.resolve_path(p) == -binding.ERR_UNSUPPORTED
@@ -75,6 +78,26 @@ def test_path_resolution():
     assert moe.resolve_path(_p(T=4096, path="stream")) == binding.PATH_STREAM
     assert moe.resolve_path(_p(T=8, path="tiled")) == binding.PATH_TILED
     assert moe.resolve_path(_p(dtype="f32")) == binding.PATH_TILED
+
+
+def test_down_parts():
+    """Partial sums only when asked for, on the tiled bf16 path, with h % 256 == 0 and
+    few down-projection row tiles (fewer than 4 per compute unit of MI355X)."""
+    P = binding.FLAG_DOWN_PARTIALS
+    assert moe.down_parts(_p(T=4096, d=4096, h=14336)) == 1
+    assert moe.down_parts(_p(T=4096, d=4096, h=14336, flags=P)) == 2
+    assert moe.down_parts(_p(T=16384, d=4096, h=14336, flags=P)) == 1   # enough tiles
+    assert moe.down_parts(_p(T=8192, d=6144, h=16384, flags=P)) == 1
+    assert moe.down_parts(_p(T=4096, d=4096, h=14336 + 128, flags=P)) == 1  # h % 256
+    assert moe.down_parts(_p(T=32, d=4096, h=14336, flags=P)) == 1      # streaming path
+    assert moe.down_parts(_p(T=32, d=4096, h=14336, flags=P, path="tiled")) == 2
+    assert moe.down_parts(_p(T=64, d=128, h=256, dtype="f32", flags=P)) == 1
+    # the layer's own workspace makes room for the partial sums it uses
+    S, d, h = 4096 * 2, 4096, 14336
+    acts = S * d * 2 + S * h * 2  # x_perm and act, bf16
+    assert moe.forward_workspace_bytes(_p(T=4096, d=d, h=h)) >= acts + 2 * S * d * 4
+    with pytest.raises(moe.MoeError):
+        moe.down_parts(_p(T=0))
 
 
 def test_null_and_alignment():

@@ -259,21 +259,25 @@ def _segments(counts):
 
 
 EXPERT_CASES = [
-    # name, path, T, d, h, counts per expert
-    ("stream_mixed", "stream", 64, 512, 640, [0, 5, 64, 1, 0, 33, 17, 2]),
-    ("stream_small", "stream", 32, 256, 384, [3, 0, 0, 16, 32, 1, 0, 4]),
-    ("stream_over64", "stream", 150, 256, 256, [150, 0, 70, 0, 0, 0, 0, 1]),
+    # name, path, T, d, h, counts per expert, flags
+    ("stream_mixed", "stream", 64, 512, 640, [0, 5, 64, 1, 0, 33, 17, 2], 0),
+    ("stream_small", "stream", 32, 256, 384, [3, 0, 0, 16, 32, 1, 0, 4], 0),
+    ("stream_over64", "stream", 150, 256, 256, [150, 0, 70, 0, 0, 0, 0, 1], 0),
     # segments longer than T are allowed by the offsets contract (up to S = T*K)
-    ("stream_segment_over_T", "stream", 40, 256, 256, [70, 0, 0, 0, 0, 0, 0, 10]),
-    ("stream_T16_segment_30", "stream", 16, 256, 256, [30, 0, 2, 0, 0, 0, 0, 0]),
-    ("tiled_mixed", "tiled", 1500, 256, 640, [0, 300, 1, 256, 513, 0, 77, 1000]),
-    ("tiled_one", "tiled", 40, 128, 128, [0, 0, 0, 0, 0, 0, 0, 1]),
-    ("tiled_d384", "tiled", 600, 384, 256, [200, 57, 0, 0, 300, 0, 1, 9]),
+    ("stream_segment_over_T", "stream", 40, 256, 256, [70, 0, 0, 0, 0, 0, 0, 10], 0),
+    ("stream_T16_segment_30", "stream", 16, 256, 256, [30, 0, 2, 0, 0, 0, 0, 0], 0),
+    ("tiled_mixed", "tiled", 1500, 256, 640, [0, 300, 1, 256, 513, 0, 77, 1000], 0),
+    ("tiled_one", "tiled", 40, 128, 128, [0, 0, 0, 0, 0, 0, 0, 1], 0),
+    ("tiled_d384", "tiled", 600, 384, 256, [200, 57, 0, 0, 300, 0, 1, 9], 0),
+    # down projection split into two partial sums over h
+    ("tiled_partials", "tiled", 600, 384, 512, [200, 57, 0, 0, 300, 0, 1, 9], 1),
+    ("tiled_partials_h1024", "tiled", 300, 256, 1024, [0, 256, 1, 0, 300, 0, 0, 40], 1),
 ]
 
 
-@pytest.mark.parametrize("name,path,T,d,h,counts", EXPERT_CASES, ids=[c[0] for c in EXPERT_CASES])
-def test_expert_steps(moe, oracle, name, path, T, d, h, counts):
+@pytest.mark.parametrize("name,path,T,d,h,counts,flags", EXPERT_CASES,
+                         ids=[c[0] for c in EXPERT_CASES])
+def test_expert_steps(moe, oracle, name, path, T, d, h, counts, flags):
     E, K = len(counts), 2
     S = T * K
     off = _segments(counts)
@@ -282,7 +286,9 @@ def test_expert_steps(moe, oracle, name, path, T, d, h, counts):
     inp = mi.make_inputs(cfg, seed=7)
     xp = inp["x"]  # [S, d] rows already "permuted"
     act_in = mi.make_act(S, h, "bf16", seed=8)
-    p = moe.problem(T, d, h, E, K, "bf16", "f32", path)
+    p = moe.problem(T, d, h, E, K, "bf16", "f32", path, flags)
+    parts = moe.down_parts(p)
+    assert parts == (2 if flags else 1)
     dev_x = parity.device_array(xp, "bf16")
     dev_off = parity.device_array(off, "i32")
     w1 = parity.device_array(inp["w1"], "bf16")
@@ -295,6 +301,9 @@ def test_expert_steps(moe, oracle, name, path, T, d, h, counts):
     act_h = mi.bf16_bits_to_f32(parity.host_array(act)).astype(np.float64)
     o_h = parity.host_array(o).astype(np.float64)
     of_h = parity.host_array(o_full).astype(np.float64)
+    if parts > 1:  # [parts, S, d] partial sums over h; the row is their sum
+        o_h = o_h.reshape(parts, S, d).sum(axis=0)
+        of_h = of_h.reshape(parts, S, d).sum(axis=0)
     for e in range(E):
         a, b = off[e], off[e + 1]
         if a == b:
@@ -329,6 +338,49 @@ def test_combine_step(moe):
         ok = slot[:, k] >= 0
         ref[ok] += w[ok, k:k + 1].astype(np.float64) * o_perm[slot[ok, k]].astype(np.float64)
     assert np.max(np.abs(y - ref)) <= 1e-6 * np.max(np.abs(ref))
+
+
+def test_combine_adds_partials(moe):
+    """With MOE_FLAG_DOWN_PARTIALS the combine reads parts x [S, d] partial sums."""
+    T, K, d, h = 300, 2, 256, 512
+    p = moe.problem(T, d, h, 8, K, "bf16", "f32", "tiled", moe.FLAG_DOWN_PARTIALS)
+    parts = moe.down_parts(p)
+    assert parts == 2
+    S = T * K
+    rng = np.random.default_rng(10)
+    o = rng.standard_normal((parts, S, d)).astype(np.float32)
+    slot = rng.permutation(S).reshape(T, K).astype(np.int32)
+    w = rng.random((T, K)).astype(np.float32)
+    y = moe.combine(p, parity.device_array(o, "f32"), parity.device_array(slot, "i32"),
+                    parity.device_array(w, "f32"))
+    torch.cuda.synchronize()
+    y = parity.host_array(y).astype(np.float64)
+    row = (o[0] + o[1]).astype(np.float64)  # float32 sum of the parts, then weighted
+    ref = sum(w[:, k:k + 1].astype(np.float64) * row[slot[:, k]] for k in range(K))
+    assert np.max(np.abs(y - ref)) <= 1e-6 * np.max(np.abs(ref))
+
+
+def test_staged_with_partials_equals_forward(moe, oracle):
+    """The staged entry points with MOE_FLAG_DOWN_PARTIALS run the same kernels as
+    moe_forward (which always allows partial sums): bit-identical outputs."""
+    cfg = mi.Config("staged", T=500, d=256, h=512, wg_std="fan_in_d")
+    inp = mi.make_inputs(cfg, seed=11)
+    y_fwd = _run_forward(moe, cfg, inp, "tiled")[0]
+    p = moe.problem(cfg.T, cfg.d, cfg.h, cfg.E, cfg.K, "bf16", "f32", "tiled",
+                    moe.FLAG_DOWN_PARTIALS)
+    assert moe.down_parts(p) == 2
+    dev = parity.upload_inputs(inp, "bf16")
+    idx, w, _ = moe.route(p, dev["x"], dev["w_g"])
+    offsets, perm, slot, x_perm = moe.permute(p, dev["x"], idx)
+    act = moe.expert_gate_up(p, x_perm, offsets, dev["w1"], dev["w3"])
+    o = moe.expert_down(p, act, offsets, dev["w2"])
+    y = moe.combine(p, o, slot, w)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (2, cfg.T * cfg.K, cfg.d)
+    assert np.array_equal(parity.host_array(y).astype(np.float64), y_fwd)
+    toks, y_ref, _, _ = _layer_ref(oracle, inp, cfg, np.arange(cfg.T), parity.host_array(idx),
+                                   parity.host_array(w))
+    parity.check_output(y_fwd[toks], y_ref, "bf16", "staged partials")
 
 
 def test_errors_raise(moe):
