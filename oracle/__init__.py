@@ -60,6 +60,10 @@ class Oracle:
         lib.oracle_down.argtypes = [i64, i64, i64, i32, vp, i32, vp, vp]
         lib.oracle_forward_tokens.argtypes = [i64, vp, i64, i64, i32, i32, i32,
                                               vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_rmsnorm.argtypes = [i64, i64, i32, vp, vp, ctypes.c_double, vp, vp]
+        lib.oracle_rmsnorm.restype = None
+        lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_round_bf16.restype = ctypes.c_uint16
         for f in (lib.oracle_logits, lib.oracle_topk, lib.oracle_set_weights,
                   lib.oracle_permute, lib.oracle_gate_up, lib.oracle_down,
                   lib.oracle_forward_tokens):
@@ -162,6 +166,36 @@ class Oracle:
                                        _p(np.ascontiguousarray(w2)), _p(idx), _p(w), _p(y))
         return y
 
+    # -- pre-norm block -----------------------------------------------------
+    def round_bf16(self, values) -> np.ndarray:
+        """bf16 bit patterns of doubles rounded once (to nearest, ties to even)."""
+        v = np.asarray(values, dtype=np.float64).ravel()
+        return np.array([self.lib.oracle_round_bf16(float(a)) for a in v],
+                        dtype=np.uint16).reshape(np.shape(values))
+
+    def rmsnorm(self, h, g, eps: float, dtype: str):
+        """(x in dtype storage [T, d], x_exact float64 [T, d]) of the block input h."""
+        h = np.ascontiguousarray(h)
+        g = np.ascontiguousarray(g)
+        T, d = h.shape
+        assert g.shape == (d,) and g.dtype == h.dtype
+        exact = np.empty((T, d), dtype=np.float64)
+        out = np.empty((T, d), dtype=h.dtype)
+        self.lib.oracle_rmsnorm(T, d, _DT[dtype], _p(h), _p(g), float(eps), _p(exact), _p(out))
+        return out, exact
+
+    def block_forward(self, inputs, K: int, dtype: str, eps: float,
+                      tokens: Optional[Sequence[int]] = None):
+        """Pre-norm block h + y(RMSNorm(h) g): inputs hold h (block input) and norm_w
+        beside the layer's weights. Returns dict(y, x, logits, idx, w, margin, tokens)."""
+        x, _ = self.rmsnorm(inputs["h"], inputs["norm_w"], eps, dtype)
+        out = self.forward(dict(inputs, x=x), K, dtype, tokens)
+        hrows = np.stack([_widen(inputs["h"][t], dtype) for t in out["tokens"]]) \
+            if len(out["tokens"]) else np.zeros((0, x.shape[1]))
+        out["y"] = hrows + out["y"]
+        out["x"] = x
+        return out
+
     def forward(self, inputs, K: int, dtype: str, tokens: Optional[Sequence[int]] = None):
         """Whole layer: returns dict(y, logits, idx, w, margin) (y for `tokens` or all)."""
         l, idx, w, margin = self.route(inputs["x"], inputs["w_g"], K, dtype)
@@ -170,6 +204,14 @@ class Oracle:
         y = self.forward_tokens(toks, inputs["x"], inputs["w1"], inputs["w3"], inputs["w2"],
                                 idx, w, dtype)
         return {"y": y, "logits": l, "idx": idx, "w": w, "margin": margin, "tokens": toks}
+
+
+def _widen(row, dtype: str) -> np.ndarray:
+    """Stored values (bf16 bits or float32) as float64, exactly."""
+    if dtype == "bf16":
+        return (np.asarray(row, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32) \
+            .astype(np.float64)
+    return np.asarray(row, dtype=np.float32).astype(np.float64)
 
 
 _DEFAULT: Optional[Oracle] = None

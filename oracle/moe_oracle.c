@@ -21,6 +21,15 @@
  * The permute step (gather each expert's tokens into one contiguous segment,
  * ml-canon page, "Questions worth asking") is written as a stable counting sort.
  *
+ * Around the layer (the pre-norm block): the pages build Mixtral on a
+ * LLaMA-like architecture with RMSNorm (ml-canon "52 Mixtral", Connections),
+ * which normalises the block input before the feed-forward layer; the block
+ * output adds the layer's output to that input (the residual path):
+ *   x = h / sqrt(mean_j h_j^2 + eps) * g,   out = h + y(x)
+ * The pages give no formula or epsilon for RMSNorm; this is its standard form
+ * with a caller-given eps. x is rounded once to the layer's input type (it is
+ * the layer's input x), here directly from the double value.
+ *
  * Every value is widened exactly to double (bf16 bits << 16, or float); every
  * dot product is summed in ascending index order. A product of two bf16 or two
  * fp32 values is exact in double, so contraction into fused multiply-add cannot
@@ -372,4 +381,64 @@ void oracle_forward_tokens(int64_t n, const int64_t *tokens, int64_t d, int64_t 
   free(bstart);
   free(bexp);
   free(order);
+}
+
+/*
+ * Round a double once to the nearest bfloat16 (8 significant bits), ties to
+ * even; returns the bit pattern. Finite inputs in the normal range of bf16.
+ */
+uint16_t oracle_round_bf16(double v) {
+  if (v == 0.0) return signbit(v) ? 0x8000u : 0u;
+  int e;
+  double f = frexp(fabs(v), &e); /* |v| = f * 2^e, f in [0.5, 1) */
+  double m = ldexp(f, 8);        /* [128, 256): 8 significant bits kept */
+  double r = nearbyint(m);       /* default rounding mode: to nearest, ties to even */
+#if ORACLE_MUTANT == 13
+  r = floor(m + 0.5); /* ties away from zero */
+#endif
+  double q = ldexp(r, e - 8);
+  float qf = (float)q; /* exact: q has at most 9 significant bits */
+  if (v < 0) qf = -qf;
+  uint32_t u;
+  memcpy(&u, &qf, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+/*
+ * RMSNorm of T rows of d values (see the header):
+ *   x_exact[t, j] = h[t, j] / sqrt(mean_j' h[t, j']^2 + eps) * g[j]  (double)
+ *   x_out[t, j]   = x_exact rounded once to dt (bf16 bits or float)
+ * Sums in ascending index order.
+ */
+void oracle_rmsnorm(int64_t T, int64_t d, int32_t dt, const void *h, const void *g, double eps,
+                    double *x_exact, void *x_out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int64_t j = 0; j < d; ++j) {
+      double v = ld(h, dt, (size_t)(t * d + j));
+      ss += v * v;
+    }
+#if ORACLE_MUTANT == 10
+    double inv = 1.0 / sqrt(ss / (double)d);
+    (void)eps;
+#elif ORACLE_MUTANT == 11
+    double inv = 1.0 / sqrt(ss + eps);
+#else
+    double inv = 1.0 / sqrt(ss / (double)d + eps);
+#endif
+    for (int64_t j = 0; j < d; ++j) {
+#if ORACLE_MUTANT == 12
+      double xv = ld(h, dt, (size_t)(t * d + j)) * inv;
+      (void)g;
+#else
+      double xv = ld(h, dt, (size_t)(t * d + j)) * inv * ld(g, dt, (size_t)j);
+#endif
+      x_exact[t * d + j] = xv;
+      if (dt == ORACLE_BF16)
+        ((uint16_t *)x_out)[t * d + j] = oracle_round_bf16(xv);
+      else
+        ((float *)x_out)[t * d + j] = (float)xv;
+    }
+  }
 }

@@ -290,4 +290,88 @@ def pin_token_subset_consistent(o):
     assert np.array_equal(part["y"], full["y"][sub])
 
 
+# --- pre-norm block (RMSNorm before the layer, residual after) ------------------
+
+def pin_rmsnorm_matches_torch(o):
+    """RMSNorm of the block input (ml-canon page "52 Mixtral", Connections: the
+    LLaMA-like blocks use RMSNorm) equals torch's float64 rms_norm on exactly
+    widened inputs, for bf16 and fp32 storage, with a large and a small eps."""
+    import torch
+
+    rng = _rng(21)
+    for dt in ("bf16", "f32"):
+        for eps in (1e-5, 0.5):
+            if dt == "bf16":
+                h, g = _rand_bf16(rng, (9, 96)), _rand_bf16(rng, (96,), 0.7)
+            else:
+                h, g = _rand_f32(rng, (9, 96)), _rand_f32(rng, (96,), 0.7)
+            _, exact = o.rmsnorm(h, g, eps, dt)
+            ref = torch.nn.functional.rms_norm(torch.from_numpy(to_float64(h, dt)), (96,),
+                                               torch.from_numpy(to_float64(g, dt)), eps).numpy()
+            _close(exact, ref, 1e-14, f"rmsnorm {dt} eps={eps}")
+
+
+def pin_rmsnorm_closed_forms(o):
+    """Closed forms: a constant row c gives g * c / sqrt(c^2 + eps); a one-hot row
+    a * e_j gives g_j * a / sqrt(a^2 / d + eps) at j and 0 elsewhere; with g = 1 and
+    eps = 0 every row has mean square 1; scaling a row by s > 0 (eps = 0) changes
+    nothing; negating it negates the output."""
+    rng = _rng(22)
+    d = 64
+    g = _rand_f32(rng, (d,), 1.0)
+    for c, eps in ((3.0, 1.0), (-0.25, 0.0625)):
+        h = np.full((1, d), c, dtype=np.float32)
+        _, x = o.rmsnorm(h, g, eps, "f32")
+        _close(x[0], g.astype(np.float64) * c / np.sqrt(c * c + eps), 1e-15, "constant row")
+    h = np.zeros((1, d), dtype=np.float32)
+    h[0, 5] = 2.0
+    _, x = o.rmsnorm(h, g, 0.5, "f32")
+    want = np.zeros(d)
+    want[5] = float(g[5]) * 2.0 / np.sqrt(4.0 / d + 0.5)
+    _close(x[0], want, 1e-15, "one-hot row")
+    h = _rand_f32(rng, (7, d))
+    _, x = o.rmsnorm(h, np.ones(d, dtype=np.float32), 0.0, "f32")
+    assert np.max(np.abs(np.mean(x * x, axis=1) - 1.0)) < 1e-14, "unit mean square"
+    _, xs = o.rmsnorm((h * np.float32(4.0)).astype(np.float32), g, 0.0, "f32")
+    _, x1 = o.rmsnorm(h, g, 0.0, "f32")
+    _close(xs, x1, 1e-15, "scale invariance")
+    _, xn = o.rmsnorm(-h, g, 0.0, "f32")
+    assert np.array_equal(xn, -x1), "sign symmetry"
+
+
+def pin_round_bf16_nearest_even(o):
+    """The once-rounded bf16 values: exact values stay, a tie between two bf16
+    neighbours goes to the one with an even last bit, anything else to the nearer
+    one (hand-derived bit patterns)."""
+    cases = [(1.0, 0x3F80), (1.0 + 2.0 ** -8, 0x3F80), (1.0 + 3 * 2.0 ** -8, 0x3F82),
+             (1.0 + 2.0 ** -8 + 2.0 ** -30, 0x3F81), (-(1.0 + 2.0 ** -8), 0xBF80),
+             (3.0, 0x4040), (0.1, 0x3DCD), (-2.0 ** -10, 0xBA80), (0.0, 0x0000),
+             (255.5, 0x4380), (65280.0 + 128.0, 0x4780), (65280.0 + 127.0, 0x477F)]
+    got = o.round_bf16([c[0] for c in cases])
+    for (v, want), gbits in zip(cases, got):
+        assert int(gbits) == want, f"round_bf16({v!r}) = {int(gbits):#06x}, want {want:#06x}"
+    # x stored in bf16 is the once-rounded exact value
+    rng = _rng(23)
+    h, g = _rand_bf16(rng, (3, 32)), _rand_bf16(rng, (32,))
+    xb, exact = o.rmsnorm(h, g, 1e-5, "bf16")
+    assert np.array_equal(xb, o.round_bf16(exact))
+
+
+def pin_block_residual(o):
+    """The pre-norm block returns its input plus the layer's output on the
+    normalised input: with every W2 = 0 the layer adds nothing and the block is the
+    identity; otherwise block - input equals the plain layer on x = RMSNorm(h)."""
+    rng = _rng(24)
+    inp = _tiny_layer(rng, 12, 32, 48, 8, "bf16")
+    inp["h"] = _rand_bf16(rng, (12, 32), 2.0)
+    inp["norm_w"] = _rand_bf16(rng, (32,), 0.5)
+    zero = dict(inp, w2=np.zeros_like(inp["w2"]))
+    out = o.block_forward(zero, 2, "bf16", 1e-5)
+    assert np.array_equal(out["y"], to_float64(inp["h"], "bf16"))
+    out = o.block_forward(inp, 2, "bf16", 1e-5)
+    plain = o.forward(dict(inp, x=out["x"]), 2, "bf16")
+    assert np.array_equal(out["y"], to_float64(inp["h"], "bf16") + plain["y"])
+    assert np.array_equal(out["idx"], plain["idx"])
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
