@@ -46,6 +46,9 @@ def parse():
                     help="approximate budget of the CPU-oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "stream", "tiled"])
+    ap.add_argument("--block", action="store_true",
+                    help="time the pre-norm block instead of the bare layer: RMSNorm of the "
+                         "block input before routing, the residual added in the combine")
     ap.add_argument("--sweep", default="",
                     help="comma-separated batch sizes T: time moe_forward on both expert paths "
                          "at each T with the workload's d, h and distributions (prints one JSON "
@@ -202,13 +205,25 @@ def main():
     act = torch.empty((S, h), dtype=dt, device="cuda")
     o_perm = torch.empty((S, d) if parts == 1 else (parts, S, d), dtype=f32, device="cuda")
     y = torch.empty((T, d), dtype=f32, device="cuda")
+    BLOCK_EPS = 1e-5
+    if args.block:
+        blk = mi.make_block(cfg, seed=0)
+        h_in = parity.device_array(blk["h"], cfg.dtype)
+        norm_w = parity.device_array(blk["norm_w"], cfg.dtype)
+        x_in = torch.empty((T, d), dtype=dt, device="cuda")  # normalised block input
+    else:
+        x_in = dev["x"]
 
     def step(i, ev=None, gu=None):
         ws = wsets[i % copies]
         if ev is not None:
             ev[0].record()
-        moe.route(p, dev["x"], dev["w_g"], idx, w)
-        moe.permute(p, dev["x"], idx, offsets, perm, slot, x_perm)
+        if args.block:
+            moe.rmsnorm(p, h_in, norm_w, BLOCK_EPS, x_in)
+            if ev is not None:
+                ev[5].record()
+        moe.route(p, x_in, dev["w_g"], idx, w)
+        moe.permute(p, x_in, idx, offsets, perm, slot, x_perm)
         if ev is not None:
             ev[1].record()
         if gu is not None:
@@ -221,7 +236,10 @@ def main():
         moe.expert_down(p, act, offsets, ws["w2"], o_perm)
         if ev is not None:
             ev[3].record()
-        moe.combine(p, o_perm, slot, w, y)
+        if args.block:
+            moe.combine_residual(p, o_perm, slot, w, h_in, y)
+        else:
+            moe.combine(p, o_perm, slot, w, y)
         if ev is not None:
             ev[4].record()
 
@@ -249,25 +267,34 @@ def main():
     # Stage breakdown: a separate, shorter pass with events between all stages
     # (events add a few microseconds each, so this pass is not the timed one).
     n_diag = max(3, min(args.steps, 30))
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_diag)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_diag)]
     for i in range(n_diag):
         step(i, events[i])
     torch.cuda.synchronize()
     stage = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(4)] for ev in events])
     stage_ms = stage.mean(axis=0)
+    norm_ms = float(np.mean([ev[0].elapsed_time(ev[5]) for ev in events])) if args.block else None
     gpu_ms_step = float(np.mean([ev[0].elapsed_time(ev[4]) for ev in events]))
 
     # one-call API on the same inputs, for comparison (not part of the timed region)
-    ws_fwd = torch.empty((moe.forward_workspace_bytes(p),), dtype=torch.uint8, device="cuda")
+    if args.block:
+        ws_fwd = torch.empty((moe.block_workspace_bytes(p),), dtype=torch.uint8, device="cuda")
+
+        def one_call(ws_):
+            moe.block_forward(p, h_in, norm_w, BLOCK_EPS, dev["w_g"], ws_["w1"], ws_["w3"],
+                              ws_["w2"], y, ws=ws_fwd)
+    else:
+        ws_fwd = torch.empty((moe.forward_workspace_bytes(p),), dtype=torch.uint8, device="cuda")
+
+        def one_call(ws_):
+            moe.forward(p, dev["x"], dev["w_g"], ws_["w1"], ws_["w3"], ws_["w2"], y, ws=ws_fwd)
     for _ in range(3):
-        moe.forward(p, dev["x"], dev["w_g"], wsets[0]["w1"], wsets[0]["w3"], wsets[0]["w2"], y,
-                    ws=ws_fwd)
+        one_call(wsets[0])
     torch.cuda.synchronize()
     n_fwd = max(5, min(args.steps, 50))
     t1 = time.perf_counter()
     for i in range(n_fwd):
-        ws_ = wsets[i % copies]
-        moe.forward(p, dev["x"], dev["w_g"], ws_["w1"], ws_["w3"], ws_["w2"], y, ws=ws_fwd)
+        one_call(wsets[i % copies])
     torch.cuda.synchronize()
     ms_forward = (time.perf_counter() - t1) * 1e3 / n_fwd
 
@@ -325,7 +352,11 @@ def main():
         c0 = time.perf_counter()
         passes = 0
         while True:
-            xs = np.ascontiguousarray(inp["x"][:n])
+            if args.block:
+                xs, _ = o.rmsnorm(np.ascontiguousarray(blk["h"][:n]), blk["norm_w"], BLOCK_EPS,
+                                  cfg.dtype)
+            else:
+                xs = np.ascontiguousarray(inp["x"][:n])
             l, idx_r, w_r, margin = o.route(xs, inp["w_g"], K, cfg.dtype)
             y_ref = o.forward_tokens(toks, xs, inp["w1"], inp["w3"], inp["w2"], idx_r, w_r,
                                      cfg.dtype)
@@ -336,15 +367,22 @@ def main():
         cpu = {"value": round(n / cpu_s, 3), "unit": "tokens/s", "cores": o.threads,
                "kind": "oracle",
                "sample": f"first {n} of {T} tokens of {cfg.name} (route + all K experts + "
-                         f"combine, float64), {passes} pass(es), {cpu_s:.2f} s per pass"}
+                         f"combine{', with the RMSNorm and residual of the block' if args.block else ''}"
+                         f", float64), {passes} pass(es), {cpu_s:.2f} s per pass"}
         # parity of the timed run's output on the same tokens (rule R applied)
         ih = parity.host_array(idx)[:n]
         wh = parity.host_array(w)[:n]
-        idx_eval, diff = parity.check_routing(ih, wh, l, idx_r, margin, K, o)
+        # (block: x is normalised in float32 on the GPU and in float64 here, both rounded
+        # once to bf16, so routing is compared with the block's wider near-tie margin)
+        tol = dict(tie_margin=1e-2, w_tol=2e-3) if args.block and cfg.dtype == "bf16" else {}
+        idx_eval, diff = parity.check_routing(ih, wh, l, idx_r, margin, K, o, **tol)
         if len(diff):
             y_ref = o.forward_tokens(toks, xs, inp["w1"], inp["w3"], inp["w2"], idx_eval,
                                      o.set_weights(l, idx_eval), cfg.dtype)
-        spot_rel = parity.check_output(parity.host_array(y)[:n], y_ref, cfg.dtype, "bench")
+        y_gpu = parity.host_array(y)[:n].astype(np.float64)
+        if args.block:  # compare the MoE part; the residual is added exactly in float32
+            y_gpu = y_gpu - mi.to_float64(blk["h"][:n], cfg.dtype)
+        spot_rel = parity.check_output(y_gpu, y_ref, cfg.dtype, "bench")
         spot = {"tokens": n, "max_err_over_rms": float(f"{spot_rel:.4e}"),
                 "tolerance": parity.Y_TOL[cfg.dtype]}
 
@@ -362,15 +400,23 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded generator; random-init weights of the layer's shape)",
         "config": {"workload": cfg.name, "T": T, "d": d, "h": h, "E": E, "K": K,
-                   "path": path, "down_partial_sums": parts, "weight_copies": copies},
+                   "path": path, "down_partial_sums": parts, "weight_copies": copies,
+                   "block": bool(args.block)},
         "roofline": roof,
         "layer": layer,
         "cpu_baseline": cpu,
-        "stages_ms": {"route+permute": round(float(stage_ms[0]), 5),
+        "stages_ms": {("rmsnorm+route+permute" if args.block else "route+permute"):
+                      round(float(stage_ms[0]), 5),
                       "gate_up": round(float(stage_ms[1]), 5),
                       "down": round(float(stage_ms[2]), 5),
                       "combine": round(float(stage_ms[3]), 5)},
         "gpu_ms_per_step_events": round(gpu_ms_step, 5),
+        "block_rmsnorm": None if norm_ms is None else {
+            "ms": round(norm_ms, 5),
+            "hbm_bytes": T * d * es * 2 + d * es,
+            "achieved_GBps": round((T * d * es * 2 + d * es) / (norm_ms / 1e3) / 1e9, 1),
+            "frac_of_hbm_peak": round((T * d * es * 2 + d * es) / (norm_ms / 1e3) / 1e9
+                                      / HBM_PEAK_GBS, 4)},
         "stages_note": f"separate pass of {n_diag} steps with events between the stages",
         "ms_per_step_one_call_api": round(ms_forward, 5),
         "rows_per_expert": counts.tolist(),

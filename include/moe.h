@@ -183,6 +183,43 @@ moe_status moe_expert_swiglu(const moe_problem *p, const void *x_perm, const int
 moe_status moe_combine(const moe_problem *p, const float *o_perm, const int32_t *slot_pos,
                        const float *topk_w, void *y, void *stream);
 
+/*
+ * Combine plus a residual: y[t] = residual[t] + sum_k topk_w[t, k] * o_perm[...],
+ * the weighted sum formed as in moe_combine and added to the residual in
+ * float32 before the single rounding to out_dtype.
+ *   residual [T, d]  dtype (the input of a pre-norm block)
+ */
+moe_status moe_combine_residual(const moe_problem *p, const float *o_perm,
+                                const int32_t *slot_pos, const float *topk_w,
+                                const void *residual, void *y, void *stream);
+
+/*
+ * RMSNorm of the block input, the normalisation in front of the MoE layer in
+ * Mixtral's LLaMA-like blocks (ml-canon page "52 Mixtral", Connections; the
+ * pages name RMSNorm but give no formula or epsilon, so this is its standard
+ * form with a caller-given eps):
+ *   x[t, j] = h[t, j] / sqrt(mean_j' h[t, j']^2 + eps) * norm_w[j]
+ * The mean square and the scaling are float32; x is rounded once to dtype.
+ *   h [T, d] dtype, norm_w [d] dtype, x [T, d] dtype out; eps finite, > 0
+ *   (MOE_ERR_UNSUPPORTED otherwise).
+ */
+moe_status moe_rmsnorm(const moe_problem *p, const void *h, const void *norm_w, float eps,
+                       void *x, void *stream);
+
+/* Bytes of workspace moe_block_forward needs (0 if `p` is invalid). */
+size_t moe_block_workspace_bytes(const moe_problem *p);
+
+/*
+ * The pre-norm block around the layer: y = h + MoE(RMSNorm(h) * norm_w), i.e.
+ * moe_rmsnorm, then the layer of moe_forward on the normalised x (kept in `ws`),
+ * with the residual added in the combine step. Arguments as for moe_rmsnorm and
+ * moe_forward; ws: at least moe_block_workspace_bytes(p), 256-byte aligned.
+ */
+moe_status moe_block_forward(const moe_problem *p, const void *h, const void *norm_w, float eps,
+                             const void *w_g, const void *w1, const void *w3, const void *w2,
+                             void *y, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                             void *stream);
+
 /* Bytes of workspace moe_forward needs (0 if `p` is invalid). */
 size_t moe_forward_workspace_bytes(const moe_problem *p);
 

@@ -216,6 +216,17 @@ def make_act(n: int, h: int, dtype: str, seed: int = 0, std: float = 1.0) -> np.
     return _store(_normal(child, (n, h), std), dtype)
 
 
+def make_block(cfg: Config, seed: int = 0, h_std: float = 2.0,
+               w_std: float = 0.1) -> Dict[str, np.ndarray]:
+    """Inputs of a pre-norm block around the layer: the block input h [T, d]
+    (standard normal times h_std) and the norm gain norm_w [d] (1 + standard
+    normal times w_std), stored in cfg.dtype. Streams SeedSequence([seed, 0xB10C])."""
+    kids = np.random.SeedSequence([seed, 0xB10C]).spawn(2)
+    h = _normal(kids[0], (cfg.T, cfg.d), h_std)
+    g = (1.0 + _normal(kids[1], (cfg.d,), w_std)).astype(np.float32)
+    return {"h": _store(h, cfg.dtype), "norm_w": _store(g, cfg.dtype)}
+
+
 def make_routing(T: int, E: int, K: int, seed: int = 0) -> np.ndarray:
     """Random distinct expert ids per token, [T, K] int32 (for the permute alone)."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x9E7])))

@@ -8,14 +8,15 @@ Python binding (torch tensors in, torch tensors out).
 """
 from .binding import (  # noqa: F401
     BF16, F32, FLAG_DOWN_PARTIALS, PATH_AUTO, PATH_STREAM, PATH_TILED, MoeError, Problem,
-    combine, down_parts, expert_down, expert_gate_up, expert_swiglu, expert_workspace_bytes,
-    forward, forward_workspace_bytes, header_functions, last_error, lib, permute, problem,
-    resolve_path, route, status_string,
+    block_forward, block_workspace_bytes, combine, combine_residual, down_parts, expert_down,
+    expert_gate_up, expert_swiglu, expert_workspace_bytes, forward, forward_workspace_bytes,
+    header_functions, last_error, lib, permute, problem, resolve_path, rmsnorm, route,
+    status_string,
 )
 
 __all__ = [
     "Problem", "problem", "route", "permute", "expert_gate_up", "expert_down", "expert_swiglu",
     "combine", "forward", "expert_workspace_bytes", "forward_workspace_bytes", "resolve_path",
-    "down_parts",
+    "down_parts", "rmsnorm", "combine_residual", "block_forward", "block_workspace_bytes",
     "MoeError", "status_string", "last_error", "header_functions",
 ]

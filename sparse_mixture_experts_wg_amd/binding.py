@@ -61,7 +61,7 @@ def _load() -> ctypes.CDLL:
 
     if not os.path.exists(LIBRARY):
         raise ImportError(f"{LIBRARY} is not built; run __graft_entry__.build() or "
-                          "python -m sparse_mixture_experts_wg_amd.build")
+                          "python sparse_mixture_experts_wg_amd/build.py")
     lib = ctypes.CDLL(LIBRARY)
     P, vp, i32 = ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_int
     sz = ctypes.c_size_t
@@ -79,6 +79,11 @@ def _load() -> ctypes.CDLL:
         "moe_combine": ([P, vp, vp, vp, vp, vp], i32),
         "moe_forward_workspace_bytes": ([P], sz),
         "moe_forward": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_rmsnorm": ([P, vp, vp, ctypes.c_float, vp, vp], i32),
+        "moe_combine_residual": ([P, vp, vp, vp, vp, vp, vp], i32),
+        "moe_block_workspace_bytes": ([P], sz),
+        "moe_block_forward": ([P, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+                              i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -242,6 +247,55 @@ def expert_swiglu(p: Problem, x_perm, offsets, w1, w3, w2, o_perm=None, ws=None,
                                  _ptr(o_perm, "o_perm", o_shape, torch.float32), _ptr(ws, "ws"),
                                  ws.numel() * ws.element_size(), _stream(stream)))
     return o_perm
+
+
+def block_workspace_bytes(p: Problem) -> int:
+    return lib.moe_block_workspace_bytes(ctypes.byref(p))
+
+
+def rmsnorm(p: Problem, h, norm_w, eps: float, x=None, stream=None):
+    T, d = int(p.T), int(p.d)
+    dt = _tdtype(p.dtype)
+    x = _empty((T, d), dt, h) if x is None else x
+    _check(lib.moe_rmsnorm(ctypes.byref(p), _ptr(h, "h", (T, d), dt),
+                           _ptr(norm_w, "norm_w", (d,), dt), ctypes.c_float(eps),
+                           _ptr(x, "x", (T, d), dt), _stream(stream)))
+    return x
+
+
+def combine_residual(p: Problem, o_perm, slot_pos, topk_w, residual, y=None, stream=None):
+    torch = _torch()
+    T, d, K = int(p.T), int(p.d), int(p.K)
+    yd = _tdtype(p.out_dtype)
+    y = _empty((T, d), yd, o_perm) if y is None else y
+    _check(lib.moe_combine_residual(ctypes.byref(p),
+                                    _ptr(o_perm, "o_perm", _o_shape(p), torch.float32),
+                                    _ptr(slot_pos, "slot_pos", (T, K), torch.int32),
+                                    _ptr(topk_w, "topk_w", (T, K), torch.float32),
+                                    _ptr(residual, "residual", (T, d), _tdtype(p.dtype)),
+                                    _ptr(y, "y", (T, d), yd), _stream(stream)))
+    return y
+
+
+def block_forward(p: Problem, h, norm_w, eps: float, w_g, w1, w3, w2, y=None, topk_idx=None,
+                  topk_w=None, ws=None, stream=None):
+    """Pre-norm block: y = h + MoE(RMSNorm(h) * norm_w)."""
+    torch = _torch()
+    T, d, hd, E, K = int(p.T), int(p.d), int(p.h), int(p.E), int(p.K)
+    dt = _tdtype(p.dtype)
+    yd = _tdtype(p.out_dtype)
+    y = _empty((T, d), yd, h) if y is None else y
+    need = block_workspace_bytes(p)
+    ws = _empty((max(need, 1),), torch.uint8, h) if ws is None else ws
+    _check(lib.moe_block_forward(ctypes.byref(p), _ptr(h, "h", (T, d), dt),
+                                 _ptr(norm_w, "norm_w", (d,), dt), ctypes.c_float(eps),
+                                 _ptr(w_g, "w_g", (d, E), dt), _ptr(w1, "w1", (E, hd, d), dt),
+                                 _ptr(w3, "w3", (E, hd, d), dt), _ptr(w2, "w2", (E, d, hd), dt),
+                                 _ptr(y, "y", (T, d), yd),
+                                 _ptr(topk_idx, "topk_idx", (T, K), torch.int32),
+                                 _ptr(topk_w, "topk_w", (T, K), torch.float32), _ptr(ws, "ws"),
+                                 ws.numel() * ws.element_size(), _stream(stream)))
+    return y
 
 
 def combine(p: Problem, o_perm, slot_pos, topk_w, y=None, stream=None):

@@ -1,6 +1,6 @@
 """Build libmoe.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-    python -m sparse_mixture_experts_wg_amd.build
+    python sparse_mixture_experts_wg_amd/build.py
 
 Objects go to sparse_mixture_experts_wg_amd/_build/, the library to
 sparse_mixture_experts_wg_amd/libmoe.so (both in-tree, both git-ignored).
@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libmoe.so")
 
 ARCH = "gfx950"
-SOURCES = ["abi.cpp", "route.hip", "permute.hip", "combine.hip", "gemm_f32.hip",
+SOURCES = ["abi.cpp", "norm.hip", "route.hip", "permute.hip", "combine.hip", "gemm_f32.hip",
            "gemm_stream.hip", "gemm_tiled.hip"]
 
 

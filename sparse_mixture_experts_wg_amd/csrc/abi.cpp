@@ -148,6 +148,18 @@ hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
 // ---- the steps, after validation ----------------------------------------------
 
+moe_status check_eps(float eps) {
+  if (!(eps > 0.0f) || !(eps < 1e30f))
+    return fail(MOE_ERR_UNSUPPORTED, "eps=%g: must be finite and > 0", double(eps));
+  return MOE_OK;
+}
+
+moe_status do_rmsnorm(const moe_problem *p, const void *h, const void *g, float eps, void *x,
+                      hipStream_t s) {
+  return hip_result(moe::launch_rmsnorm(p->dtype == MOE_BF16, h, g, eps, p->T, int(p->d), x, s),
+                    "rmsnorm launch");
+}
+
 moe_status do_route(const moe_problem *p, const void *x, const void *w_g, int32_t *idx, float *w,
                     float *logits, hipStream_t s) {
   return hip_result(moe::launch_route(p->dtype == MOE_BF16, x, w_g, p->T, int(p->d), p->E, p->K,
@@ -198,9 +210,10 @@ moe_status do_down(const moe_problem *p, const void *act, const int32_t *offsets
 }
 
 moe_status do_combine(const moe_problem *p, const float *o_perm, int parts, const int32_t *slot,
-                      const float *w, void *y, hipStream_t s) {
+                      const float *w, const void *residual, void *y, hipStream_t s) {
   return hip_result(moe::launch_combine(o_perm, parts, slot, w, p->T, p->K, int(p->d),
-                                        p->out_dtype == MOE_BF16, y, s),
+                                        p->out_dtype == MOE_BF16, residual,
+                                        p->dtype == MOE_BF16, y, s),
                     "combine launch");
 }
 
@@ -213,6 +226,46 @@ moe_status guarded(F &&f) {
   } catch (...) {
     return fail(MOE_ERR_HIP, "internal error");
   }
+}
+
+// Arguments of the whole layer besides x; nothing is enqueued before they pass.
+moe_status check_layer_args(const void *w_g, const void *w1, const void *w3, const void *w2,
+                            const void *y, const int32_t *topk_idx, const float *topk_w,
+                            const void *ws) {
+  CHECK(check_ptr(w_g, "w_g"));
+  CHECK(check_ptr(w1, "w1"));
+  CHECK(check_ptr(w3, "w3"));
+  CHECK(check_ptr(w2, "w2"));
+  CHECK(check_ptr(y, "y"));
+  CHECK(check_ptr(topk_idx, "topk_idx", false));
+  CHECK(check_ptr(topk_w, "topk_w", false));
+  CHECK(check_ptr(ws, "ws"));
+  if (reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(MOE_ERR_ALIGN, "ws is not 256-byte aligned");
+  return MOE_OK;
+}
+
+// The whole layer on checked arguments; `residual` (nullable) is added to y.
+moe_status run_layer(const moe_problem *p, const void *x, const void *w_g, const void *w1,
+                     const void *w3, const void *w2, const void *residual, void *y,
+                     int32_t *topk_idx, float *topk_w, void *ws, void *stream) {
+  const ForwardLayout L = forward_layout(p);
+  char *base = static_cast<char *>(ws);
+  int32_t *idx = topk_idx ? topk_idx : reinterpret_cast<int32_t *>(base + L.idx);
+  float *w = topk_w ? topk_w : reinterpret_cast<float *>(base + L.w);
+  int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+  int32_t *perm = reinterpret_cast<int32_t *>(base + L.perm);
+  int32_t *slot = reinterpret_cast<int32_t *>(base + L.slot);
+  void *x_perm = base + L.x_perm;
+  void *act = base + L.act;
+  float *o_perm = reinterpret_cast<float *>(base + L.o_perm);
+  const hipStream_t s = as_stream(stream);
+  CHECK(do_route(p, x, w_g, idx, w, nullptr, s));
+  CHECK(do_permute(p, x, idx, offsets, perm, slot, x_perm, s));
+  CHECK(do_gate_up(p, x_perm, offsets, w1, w3, act, s));
+  CHECK(do_down(p, act, offsets, w2, o_perm, L.parts, s));
+  CHECK(do_combine(p, o_perm, L.parts, slot, w, residual, y, s));
+  return ok();
 }
 
 }  // namespace
@@ -338,7 +391,7 @@ moe_status moe_combine(const moe_problem *p, const float *o_perm, const int32_t 
     CHECK(check_ptr(slot_pos, "slot_pos"));
     CHECK(check_ptr(topk_w, "topk_w"));
     CHECK(check_ptr(y, "y"));
-    CHECK(do_combine(p, o_perm, down_parts(p), slot_pos, topk_w, y, as_stream(stream)));
+    CHECK(do_combine(p, o_perm, down_parts(p), slot_pos, topk_w, nullptr, y, as_stream(stream)));
     return ok();
   });
 }
@@ -354,35 +407,65 @@ moe_status moe_forward(const moe_problem *p, const void *x, const void *w_g, con
   return guarded([&] {
     CHECK(check_problem(p));
     CHECK(check_ptr(x, "x"));
-    CHECK(check_ptr(w_g, "w_g"));
-    CHECK(check_ptr(w1, "w1"));
-    CHECK(check_ptr(w3, "w3"));
-    CHECK(check_ptr(w2, "w2"));
-    CHECK(check_ptr(y, "y"));
-    CHECK(check_ptr(topk_idx, "topk_idx", false));
-    CHECK(check_ptr(topk_w, "topk_w", false));
-    CHECK(check_ptr(ws, "ws"));
-    if (reinterpret_cast<uintptr_t>(ws) % 256)
-      return fail(MOE_ERR_ALIGN, "ws is not 256-byte aligned");
-    const ForwardLayout L = forward_layout(p);
-    if (ws_bytes < L.total)
-      return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
-    char *base = static_cast<char *>(ws);
-    int32_t *idx = topk_idx ? topk_idx : reinterpret_cast<int32_t *>(base + L.idx);
-    float *w = topk_w ? topk_w : reinterpret_cast<float *>(base + L.w);
-    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
-    int32_t *perm = reinterpret_cast<int32_t *>(base + L.perm);
-    int32_t *slot = reinterpret_cast<int32_t *>(base + L.slot);
-    void *x_perm = base + L.x_perm;
-    void *act = base + L.act;
-    float *o_perm = reinterpret_cast<float *>(base + L.o_perm);
-    const hipStream_t s = as_stream(stream);
-    CHECK(do_route(p, x, w_g, idx, w, nullptr, s));
-    CHECK(do_permute(p, x, idx, offsets, perm, slot, x_perm, s));
-    CHECK(do_gate_up(p, x_perm, offsets, w1, w3, act, s));
-    CHECK(do_down(p, act, offsets, w2, o_perm, L.parts, s));
-    CHECK(do_combine(p, o_perm, L.parts, slot, w, y, s));
+    CHECK(check_layer_args(w_g, w1, w3, w2, y, topk_idx, topk_w, ws));
+    if (ws_bytes < forward_layout(p).total)
+      return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes,
+                  forward_layout(p).total);
+    return run_layer(p, x, w_g, w1, w3, w2, nullptr, y, topk_idx, topk_w, ws, stream);
+  });
+}
+
+moe_status moe_rmsnorm(const moe_problem *p, const void *h, const void *norm_w, float eps,
+                       void *x, void *stream) {
+  return guarded([&] {
+    CHECK(check_problem(p));
+    CHECK(check_eps(eps));
+    CHECK(check_ptr(h, "h"));
+    CHECK(check_ptr(norm_w, "norm_w"));
+    CHECK(check_ptr(x, "x"));
+    CHECK(do_rmsnorm(p, h, norm_w, eps, x, as_stream(stream)));
     return ok();
+  });
+}
+
+moe_status moe_combine_residual(const moe_problem *p, const float *o_perm,
+                                const int32_t *slot_pos, const float *topk_w,
+                                const void *residual, void *y, void *stream) {
+  return guarded([&] {
+    CHECK(check_problem(p));
+    CHECK(check_ptr(o_perm, "o_perm"));
+    CHECK(check_ptr(slot_pos, "slot_pos"));
+    CHECK(check_ptr(topk_w, "topk_w"));
+    CHECK(check_ptr(residual, "residual"));
+    CHECK(check_ptr(y, "y"));
+    CHECK(do_combine(p, o_perm, down_parts(p), slot_pos, topk_w, residual, y,
+                     as_stream(stream)));
+    return ok();
+  });
+}
+
+size_t moe_block_workspace_bytes(const moe_problem *p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return forward_layout(p).total + align256(size_t(p->T) * p->d * esize(p->dtype));
+}
+
+moe_status moe_block_forward(const moe_problem *p, const void *h, const void *norm_w, float eps,
+                             const void *w_g, const void *w1, const void *w3, const void *w2,
+                             void *y, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                             void *stream) {
+  return guarded([&] {
+    CHECK(check_problem(p));
+    CHECK(check_eps(eps));
+    CHECK(check_ptr(h, "h"));
+    CHECK(check_ptr(norm_w, "norm_w"));
+    CHECK(check_layer_args(w_g, w1, w3, w2, y, topk_idx, topk_w, ws));
+    const size_t need = moe_block_workspace_bytes(p);
+    if (ws_bytes < need)
+      return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    // the normalised input x lives after the layer's own workspace
+    void *x = static_cast<char *>(ws) + forward_layout(p).total;
+    CHECK(do_rmsnorm(p, h, norm_w, eps, x, as_stream(stream)));
+    return run_layer(p, x, w_g, w1, w3, w2, h, y, topk_idx, topk_w, ws, stream);
   });
 }
 

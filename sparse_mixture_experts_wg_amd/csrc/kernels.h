@@ -23,6 +23,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// ---- pre-norm ----------------------------------------------------------------
+// x = RMSNorm(h) * g per row of d (a multiple of 128), rounded once to the type.
+hipError_t launch_rmsnorm(bool bf16, const void *h, const void *g, float eps, int64_t T, int d,
+                          void *x, hipStream_t s);
+
 // ---- router -----------------------------------------------------------------
 hipError_t launch_route(bool bf16, const void *x, const void *wg, int64_t T, int d, int E, int K,
                         int32_t *idx, float *w, float *logits, hipStream_t s);
@@ -61,7 +66,10 @@ hipError_t launch_f32_down(const float *act, const int32_t *offsets, const float
                            float *o_perm, int E, int64_t S, int d, int h, hipStream_t s);
 
 // ---- combine ----------------------------------------------------------------
+// residual (nullable, [T, d] in the input type, bf16 if in_bf16): y = residual + the
+// weighted sum, added in float32 before the single rounding.
 hipError_t launch_combine(const float *o_perm, int parts, const int32_t *slot_pos, const float *w,
-                          int64_t T, int K, int d, bool out_bf16, void *y, hipStream_t s);
+                          int64_t T, int K, int d, bool out_bf16, const void *residual,
+                          bool in_bf16, void *y, hipStream_t s);
 
 }  // namespace moe

@@ -49,7 +49,8 @@ def upload_inputs(inp: dict, dtype: str, device="cuda") -> dict:
     return {k: device_array(v, dtype, device) for k, v in inp.items()}
 
 
-def check_routing(idx_gpu, w_gpu, logits_ref, idx_ref, margin, K, oracle):
+def check_routing(idx_gpu, w_gpu, logits_ref, idx_ref, margin, K, oracle, tie_margin=None,
+                  w_tol=None):
     """Apply rule R; returns (expert sets to evaluate the reference with, the
     tokens whose set differs from the oracle's)."""
     idx_gpu = np.asarray(idx_gpu)
@@ -59,9 +60,11 @@ def check_routing(idx_gpu, w_gpu, logits_ref, idx_ref, margin, K, oracle):
     sg = np.sort(idx_gpu, 1)
     sr = np.sort(idx_ref, 1)
     diff = np.where(np.any(sg != sr, axis=1))[0]
-    strict = diff[margin[diff] > MARGIN]
+    tie_margin = MARGIN if tie_margin is None else tie_margin
+    w_tol = W_TOL if w_tol is None else w_tol
+    strict = diff[margin[diff] > tie_margin]
     assert strict.size == 0, (
-        f"{strict.size} tokens with margin > {MARGIN} got another expert set, e.g. token "
+        f"{strict.size} tokens with margin > {tie_margin} got another expert set, e.g. token "
         f"{strict[0]}: gpu {idx_gpu[strict[0]].tolist()} oracle {idx_ref[strict[0]].tolist()} "
         f"margin {margin[strict[0]]:.3e}")
     for t in diff:
@@ -69,13 +72,13 @@ def check_routing(idx_gpu, w_gpu, logits_ref, idx_ref, margin, K, oracle):
         assert len(chosen) == K, f"token {t}: repeated expert {idx_gpu[t].tolist()}"
         lo = min(logits_ref[t, e] for e in chosen)
         hi = max((logits_ref[t, e] for e in range(E) if e not in chosen), default=-np.inf)
-        assert lo >= hi - MARGIN, f"token {t}: invalid near-tie choice {idx_gpu[t].tolist()}"
+        assert lo >= hi - tie_margin, f"token {t}: invalid near-tie choice {idx_gpu[t].tolist()}"
     assert np.all(sg[:, 1:] != sg[:, :-1]) if K > 1 else True, "repeated expert in a set"
     idx_eval = np.array(idx_ref, dtype=np.int32, copy=True)
     idx_eval[diff] = idx_gpu[diff]
     w_ref = oracle.set_weights(logits_ref, idx_gpu.astype(np.int32))
     werr = np.max(np.abs(np.asarray(w_gpu, dtype=np.float64) - w_ref))
-    assert werr <= W_TOL, f"gate weights differ by {werr:.3e} > {W_TOL}"
+    assert werr <= w_tol, f"gate weights differ by {werr:.3e} > {w_tol}"
     return idx_eval, diff
 
 

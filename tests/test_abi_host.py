@@ -100,6 +100,28 @@ def test_down_parts():
         moe.down_parts(_p(T=0))
 
 
+def test_block_entry_points_validate():
+    p = _p()
+    eps = ctypes.c_float(1e-5)
+    # eps must be finite and > 0; nothing is enqueued on failure
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        st = lib.moe_rmsnorm(ctypes.byref(p), FAKE, FAKE, ctypes.c_float(bad), FAKE, None)
+        assert st == binding.ERR_UNSUPPORTED, bad
+    assert lib.moe_rmsnorm(ctypes.byref(p), None, FAKE, eps, FAKE, None) == binding.ERR_NULL
+    assert "h" in moe.last_error()
+    assert lib.moe_combine_residual(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE,
+                                    None) == binding.ERR_NULL
+    assert "residual" in moe.last_error()
+    need = moe.block_workspace_bytes(p)
+    assert need >= moe.forward_workspace_bytes(p) + 64 * 256 * 2
+    st = lib.moe_block_forward(ctypes.byref(p), FAKE, FAKE, eps, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               None, None, FAKE, need - 1, None)
+    assert st == binding.ERR_WORKSPACE
+    st = lib.moe_block_forward(ctypes.byref(p), FAKE, None, eps, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               None, None, FAKE, need, None)
+    assert st == binding.ERR_NULL and "norm_w" in moe.last_error()
+
+
 def test_null_and_alignment():
     p = _p()
     assert lib.moe_route(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, None) == binding.ERR_NULL

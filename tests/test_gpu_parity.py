@@ -28,9 +28,10 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _layer_ref(oracle, inp, cfg, tokens, idx_gpu, w_gpu):
+def _layer_ref(oracle, inp, cfg, tokens, idx_gpu, w_gpu, **routing_tol):
     l, idx, w, margin = oracle.route(inp["x"], inp["w_g"], cfg.K, cfg.dtype)
-    idx_eval, diff = parity.check_routing(idx_gpu, w_gpu, l, idx, margin, cfg.K, oracle)
+    idx_eval, diff = parity.check_routing(idx_gpu, w_gpu, l, idx, margin, cfg.K, oracle,
+                                          **routing_tol)
     toks = np.union1d(tokens, diff).astype(np.int64)
     w_eval = oracle.set_weights(l, idx_eval)
     y_ref = oracle.forward_tokens(toks, inp["x"], inp["w1"], inp["w3"], inp["w2"], idx_eval,
@@ -381,6 +382,117 @@ def test_staged_with_partials_equals_forward(moe, oracle):
     toks, y_ref, _, _ = _layer_ref(oracle, inp, cfg, np.arange(cfg.T), parity.host_array(idx),
                                    parity.host_array(w))
     parity.check_output(y_fwd[toks], y_ref, "bf16", "staged partials")
+
+
+# ---- pre-norm block: RMSNorm before the layer, residual after ----------------------
+
+BLOCK_EPS = 1e-5
+# The GPU normalises in float32 and the oracle in float64, and each rounds x once
+# to bf16, so a few elements of x differ by one bf16 unit (test_rmsnorm_step bounds
+# how many). One such element moves a router logit by 2^-7 |x_j| |W_g[j, e]| at
+# most, so the routing of the block is compared with a near-tie margin of 1e-2 and
+# a gate-weight tolerance of 2e-3 instead of 1e-3 and 1e-5; the layer's output
+# tolerance is unchanged.
+BLOCK_ROUTING = dict(tie_margin=1e-2, w_tol=2e-3)
+
+
+@pytest.mark.parametrize("dtype,T,d", [("bf16", 33, 4096), ("bf16", 5, 128), ("f32", 17, 384)])
+def test_rmsnorm_step(moe, oracle, dtype, T, d):
+    cfg = mi.Config("rn", T=T, d=d, h=128, dtype=dtype)
+    blk = mi.make_block(cfg, seed=12)
+    p = moe.problem(T, d, 128, 8, 2, dtype, "f32")
+    x = moe.rmsnorm(p, parity.device_array(blk["h"], dtype),
+                    parity.device_array(blk["norm_w"], dtype), BLOCK_EPS)
+    torch.cuda.synchronize()
+    xg = parity.host_array(x)
+    x_ref, exact = oracle.rmsnorm(blk["h"], blk["norm_w"], BLOCK_EPS, dtype)
+    if dtype == "bf16":
+        # float32 scaling then one rounding vs the exact value rounded once: equal
+        # except where the exact value sits within float32 error of a rounding tie
+        a = xg.view(np.int16).astype(np.int32)
+        b = x_ref.view(np.int16).astype(np.int32)
+        assert np.max(np.abs(a - b)) <= 1
+        assert np.mean(a != b) < 5e-3
+    else:
+        err = np.abs(xg.astype(np.float64) - exact) / (np.abs(exact) + 1e-30)
+        assert np.max(err) <= 2e-6
+
+
+def _run_block(moe, cfg, inp, blk, path="auto", out_dtype="f32"):
+    p = moe.problem(cfg.T, cfg.d, cfg.h, cfg.E, cfg.K, cfg.dtype, out_dtype, path)
+    dev = parity.upload_inputs(inp, cfg.dtype)
+    idx = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device="cuda")
+    y = moe.block_forward(p, parity.device_array(blk["h"], cfg.dtype),
+                          parity.device_array(blk["norm_w"], cfg.dtype), BLOCK_EPS, dev["w_g"],
+                          dev["w1"], dev["w3"], dev["w2"], topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    yh = parity.host_array(y)
+    if out_dtype == "bf16":
+        yh = mi.bf16_bits_to_f32(yh)
+    return yh.astype(np.float64), parity.host_array(idx), parity.host_array(w), p, dev
+
+
+def _block_ref(oracle, inp, blk, cfg, tokens, idx_gpu, w_gpu):
+    x, _ = oracle.rmsnorm(blk["h"], blk["norm_w"], BLOCK_EPS, cfg.dtype)
+    toks, y_ref, diff, _ = _layer_ref(oracle, dict(inp, x=x), cfg, tokens, idx_gpu, w_gpu,
+                                      **(BLOCK_ROUTING if cfg.dtype == "bf16" else {}))
+    h64 = mi.to_float64(blk["h"], cfg.dtype)[toks]
+    return toks, y_ref, h64, diff
+
+
+@pytest.mark.parametrize("name,cfg,path", [
+    ("stream_T40", mi.Config("b1", T=40, d=256, h=384, wg_std="fan_in_d"), "auto"),
+    ("tiled_T300", mi.Config("b2", T=300, d=256, h=512, wg_std="fan_in_d"), "auto"),
+    ("f32_T64", mi.Config("b3", T=64, d=128, h=256, dtype="f32", w13_std="fan_in_d",
+                          w2_std="fan_in_h"), "auto"),
+], ids=["stream_T40", "tiled_T300", "f32_T64"])
+def test_block_forward(moe, oracle, name, cfg, path):
+    """y = h + MoE(RMSNorm(h) g): the MoE part within the layer's tolerance of the
+    oracle (the residual itself is added exactly in float32)."""
+    inp = mi.make_inputs(cfg, seed=13)
+    blk = mi.make_block(cfg, seed=13)
+    y, idx, w, _, _ = _run_block(moe, cfg, inp, blk, path)
+    toks, y_ref, h64, diff = _block_ref(oracle, inp, blk, cfg, np.arange(cfg.T), idx, w)
+    parity.check_output(y[toks] - h64, y_ref, cfg.dtype, f"block {name} (MoE part)")
+    # the output itself: residual + MoE part, float32 rounding of the sum only
+    assert np.max(np.abs(y[toks] - (h64 + y_ref))) <= \
+        parity.Y_TOL[cfg.dtype] * np.sqrt(np.mean(y_ref ** 2)) + 2.0 ** -23 * np.max(np.abs(h64))
+
+
+def test_block_staged_equals_one_call(moe):
+    """moe_rmsnorm + the staged layer + moe_combine_residual reproduce
+    moe_block_forward bit for bit (bf16 output too)."""
+    cfg = mi.Config("bs", T=250, d=256, h=512, wg_std="fan_in_d")
+    inp = mi.make_inputs(cfg, seed=14)
+    blk = mi.make_block(cfg, seed=14)
+    for out_dtype in ("f32", "bf16"):
+        y1, _, _, _, dev = _run_block(moe, cfg, inp, blk, "tiled", out_dtype)
+        p = moe.problem(cfg.T, cfg.d, cfg.h, cfg.E, cfg.K, "bf16", out_dtype, "tiled",
+                        moe.FLAG_DOWN_PARTIALS)
+        hdev = parity.device_array(blk["h"], "bf16")
+        x = moe.rmsnorm(p, hdev, parity.device_array(blk["norm_w"], "bf16"), BLOCK_EPS)
+        idx, w, _ = moe.route(p, x, dev["w_g"])
+        offsets, perm, slot, x_perm = moe.permute(p, x, idx)
+        act = moe.expert_gate_up(p, x_perm, offsets, dev["w1"], dev["w3"])
+        o = moe.expert_down(p, act, offsets, dev["w2"])
+        y = moe.combine_residual(p, o, slot, w, hdev)
+        torch.cuda.synchronize()
+        y2 = parity.host_array(y)
+        if out_dtype == "bf16":
+            y2 = mi.bf16_bits_to_f32(y2)
+        assert np.array_equal(y2.astype(np.float64), y1), out_dtype
+
+
+def test_block_decode_workload(moe, oracle):
+    """The pre-norm block at the Mixtral 8x7B decode shape, every token checked."""
+    cfg = mi.CONFIGS["decode_8x7b"]
+    inp = mi.make_inputs(cfg, seed=0)
+    blk = mi.make_block(cfg, seed=0)
+    y, idx, w, _, dev = _run_block(moe, cfg, inp, blk, "auto")
+    del dev
+    toks, y_ref, h64, _ = _block_ref(oracle, inp, blk, cfg, np.arange(cfg.T), idx, w)
+    parity.check_output(y[toks] - h64, y_ref, cfg.dtype, "block decode_8x7b (MoE part)")
 
 
 def test_errors_raise(moe):
