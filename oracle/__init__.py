@@ -60,6 +60,10 @@ class Oracle:
         lib.oracle_down.argtypes = [i64, i64, i64, i32, vp, i32, vp, vp]
         lib.oracle_forward_tokens.argtypes = [i64, vp, i64, i64, i32, i32, i32,
                                               vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_permute_capped.argtypes = [i64, i32, i32, vp, i64, vp, vp, vp]
+        lib.oracle_permute_capped.restype = None
+        lib.oracle_capped_weights.argtypes = [i64, i32, vp, vp, vp]
+        lib.oracle_capped_weights.restype = None
         lib.oracle_rmsnorm.argtypes = [i64, i64, i32, vp, vp, ctypes.c_double, vp, vp]
         lib.oracle_rmsnorm.restype = None
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
@@ -125,6 +129,26 @@ class Oracle:
         slot = np.empty((T, K), dtype=np.int32)
         self.lib.oracle_permute(T, E, K, _p(idx), _p(offsets), _p(perm), _p(slot))
         return offsets, perm, slot
+
+    def permute_capped(self, idx: np.ndarray, E: int, capacity: int):
+        """permute() with at most `capacity` rows per expert (earliest slots kept;
+        dropped slots get slot_pos -1); capacity <= 0 means no cap."""
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        T, K = idx.shape
+        offsets = np.empty((E + 1,), dtype=np.int32)
+        perm = np.full((T * K,), -1, dtype=np.int32)
+        slot = np.empty((T, K), dtype=np.int32)
+        self.lib.oracle_permute_capped(T, E, K, _p(idx), int(capacity), _p(offsets), _p(perm),
+                                       _p(slot))
+        return offsets, perm, slot
+
+    def capped_weights(self, slot_pos: np.ndarray, w: np.ndarray) -> np.ndarray:
+        slot_pos = np.ascontiguousarray(slot_pos, dtype=np.int32)
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        T, K = w.shape
+        out = np.empty_like(w)
+        self.lib.oracle_capped_weights(T, K, _p(slot_pos), _p(w), _p(out))
+        return out
 
     # -- expert FFN ---------------------------------------------------------
     def gate_up(self, xrows, w1e, w3e, dtype: str) -> np.ndarray:
@@ -196,14 +220,23 @@ class Oracle:
         out["x"] = x
         return out
 
-    def forward(self, inputs, K: int, dtype: str, tokens: Optional[Sequence[int]] = None):
-        """Whole layer: returns dict(y, logits, idx, w, margin) (y for `tokens` or all)."""
+    def forward(self, inputs, K: int, dtype: str, tokens: Optional[Sequence[int]] = None,
+                capacity: int = 0):
+        """Whole layer: returns dict(y, logits, idx, w, margin, tokens[, slot_pos]) (y for
+        `tokens` or all). capacity > 0 caps the rows per expert (capacity variant)."""
         l, idx, w, margin = self.route(inputs["x"], inputs["w_g"], K, dtype)
         T = inputs["x"].shape[0]
         toks = np.arange(T) if tokens is None else np.asarray(tokens)
-        y = self.forward_tokens(toks, inputs["x"], inputs["w1"], inputs["w3"], inputs["w2"],
-                                idx, w, dtype)
-        return {"y": y, "logits": l, "idx": idx, "w": w, "margin": margin, "tokens": toks}
+        out = {"logits": l, "idx": idx, "w": w, "margin": margin, "tokens": toks}
+        w_eff = w
+        if capacity > 0:
+            E = inputs["w1"].shape[0]
+            _, _, slot = self.permute_capped(idx, E, capacity)
+            w_eff = self.capped_weights(slot, w)
+            out["slot_pos"] = slot
+        out["y"] = self.forward_tokens(toks, inputs["x"], inputs["w1"], inputs["w3"],
+                                       inputs["w2"], idx, w_eff, dtype)
+        return out
 
 
 def _widen(row, dtype: str) -> np.ndarray:

@@ -30,6 +30,13 @@
  * with a caller-given eps. x is rounded once to the layer's input type (it is
  * the layer's input x), here directly from the double value.
  *
+ * Capacity variant: the pages name the capacity factor, a cap on the tokens an
+ * expert takes (ml-canon page, "Questions worth asking"), as general MoE
+ * practice. With a cap of C rows per expert, an expert keeps its C earliest
+ * slots in (token, k) order and drops the rest; a dropped slot contributes
+ * nothing to its token's output and the kept weights are not renormalised (the
+ * pages say nothing about either, this is the plain reading).
+ *
  * Every value is widened exactly to double (bf16 bits << 16, or float); every
  * dot product is summed in ascending index order. A product of two bf16 or two
  * fp32 values is exact in double, so contraction into fused multiply-add cannot
@@ -201,6 +208,51 @@ void oracle_permute(int64_t T, int32_t E, int32_t K, const int32_t *idx,
     int64_t p = next[idx[s]]++;
     perm_token[p] = (int32_t)(s / K);
     slot_pos[s] = (int32_t)p;
+  }
+}
+
+/*
+ * The same stable sort with a cap of C rows per expert (C <= 0: no cap): in
+ * ascending slot order an expert keeps a slot while it holds fewer than C, later
+ * slots get slot_pos -1 and no row. offsets count kept rows only.
+ */
+void oracle_permute_capped(int64_t T, int32_t E, int32_t K, const int32_t *idx, int64_t C,
+                           int32_t *offsets, int32_t *perm_token, int32_t *slot_pos) {
+  int64_t S = T * K;
+  int64_t seen[64], next[64];
+  for (int32_t e = 0; e < E; ++e) seen[e] = 0;
+  /* slot s is kept when fewer than C earlier slots went to its expert */
+  for (int32_t e = 0; e <= E; ++e) offsets[e] = 0;
+  for (int64_t s = 0; s < S; ++s) {
+    int32_t e = idx[s];
+#if ORACLE_MUTANT == 14
+    int keep = (C <= 0) || (seen[e] >= 0);  /* ignores the cap */
+#else
+    int keep = (C <= 0) || (seen[e] < C);
+#endif
+    seen[e]++;
+    if (keep) offsets[e + 1] += 1;
+  }
+  for (int32_t e = 0; e < E; ++e) offsets[e + 1] += offsets[e];
+  for (int32_t e = 0; e < E; ++e) {
+    next[e] = offsets[e];
+    seen[e] = 0;
+  }
+  for (int64_t s = 0; s < S; ++s) {
+    int32_t e = idx[s];
+#if ORACLE_MUTANT == 14
+    int keep = (C <= 0) || (seen[e] >= 0);
+#else
+    int keep = (C <= 0) || (seen[e] < C);
+#endif
+    seen[e]++;
+    if (keep) {
+      int64_t p = next[e]++;
+      perm_token[p] = (int32_t)(s / K);
+      slot_pos[s] = (int32_t)p;
+    } else {
+      slot_pos[s] = -1;
+    }
   }
 }
 
@@ -440,5 +492,26 @@ void oracle_rmsnorm(int64_t T, int64_t d, int32_t dt, const void *h, const void 
       else
         ((float *)x_out)[t * d + j] = (float)xv;
     }
+  }
+}
+
+/*
+ * Gate weights after the capacity cap: a dropped slot (slot_pos < 0) weighs 0,
+ * kept slots keep their weight (no renormalisation over the kept ones).
+ */
+void oracle_capped_weights(int64_t T, int32_t K, const int32_t *slot_pos, const double *w,
+                           double *w_out) {
+  for (int64_t t = 0; t < T; ++t) {
+    double kept = 0.0;
+    for (int32_t k = 0; k < K; ++k)
+      if (slot_pos[t * K + k] >= 0) kept += w[t * K + k];
+    for (int32_t k = 0; k < K; ++k) {
+      double v = slot_pos[t * K + k] >= 0 ? w[t * K + k] : 0.0;
+#if ORACLE_MUTANT == 15
+      if (kept > 0.0) v /= kept;
+#endif
+      w_out[t * K + k] = v;
+    }
+    (void)kept;
   }
 }

@@ -290,6 +290,85 @@ def pin_token_subset_consistent(o):
     assert np.array_equal(part["y"], full["y"][sub])
 
 
+# --- capacity variant (a cap on the rows per expert) ------------------------------
+
+def _brute_capped(idx, E, C):
+    """Walk the slots in (token, k) order and keep one while its expert holds < C."""
+    T, K = idx.shape
+    held = [0] * E
+    kept = []
+    for s in range(T * K):
+        e = int(idx.flat[s])
+        if C <= 0 or held[e] < C:
+            kept.append((e, s))
+        held[e] += 1
+    offsets = [0] * (E + 1)
+    for e, _ in kept:
+        offsets[e + 1] += 1
+    for e in range(E):
+        offsets[e + 1] += offsets[e]
+    slot = [-1] * (T * K)
+    perm = [-1] * (T * K)
+    nxt = offsets[:E]
+    for e, s in kept:  # kept in slot order, so each expert's rows are in slot order
+        slot[s] = nxt[e]
+        perm[nxt[e]] = s // K
+        nxt[e] += 1
+    return np.array(offsets), np.array(perm), np.array(slot).reshape(T, K)
+
+
+def pin_capacity_permute_brute_force(o):
+    """Capacity cap (ml-canon page, "Questions worth asking": a cap on the tokens per
+    expert): the capped stable sort equals a slot-by-slot walk that keeps a slot while
+    its expert holds fewer than C rows; a cap at least T (or 0) changes nothing."""
+    rng = _rng(31)
+    for (T, E, K) in ((50, 8, 2), (9, 3, 2), (17, 4, 1)):
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+        idx[: T // 3, 0] = 0  # crowd expert 0 so that caps bite
+        for C in (1, 2, 3, 7, T, 0):
+            off, perm, slot = o.permute_capped(idx, E, C)
+            boff, bperm, bslot = _brute_capped(idx, E, C)
+            assert np.array_equal(off, boff), (T, E, K, C)
+            assert np.array_equal(slot, bslot), (T, E, K, C)
+            assert np.array_equal(perm[: off[-1]], bperm[: off[-1]]), (T, E, K, C)
+            assert np.all(np.diff(off) <= (C if C > 0 else T * K))
+        off0, perm0, slot0 = o.permute(idx, E)
+        offT, permT, slotT = o.permute_capped(idx, E, T)
+        assert np.array_equal(off0, offT) and np.array_equal(perm0, permT) and \
+            np.array_equal(slot0, slotT)
+
+
+def pin_capacity_forward_drops_without_renormalising(o):
+    """Under a cap, a token's output is the sum over its kept slots of w_k E_k(x):
+    all kept = the uncapped output, one dropped = the other slot's weighted expert
+    alone (brute force with numpy), both dropped = 0."""
+    rng = _rng(32)
+    T, d, h, E, K = 24, 16, 24, 4, 2
+    inp = _tiny_layer(rng, T, d, h, E, "f32")
+    inp["w_g"][:, 0] += np.float32(3.0) * np.abs(inp["x"]).mean()  # crowd expert 0
+    full = o.forward(inp, K, "f32")
+    capped = o.forward(inp, K, "f32", capacity=5)
+    slot = capped["slot_pos"]
+    x64 = _f64(inp, "f32")
+    n_one = n_both = 0
+    for t in range(T):
+        kept = [k for k in range(K) if slot[t, k] >= 0]
+        if len(kept) == K:
+            assert np.array_equal(capped["y"][t], full["y"][t])
+        elif not kept:
+            assert np.all(capped["y"][t] == 0.0)
+            n_both += 1
+        else:
+            k = kept[0]
+            e = int(full["idx"][t, k])
+            want = full["w"][t, k] * ref_numpy.dense_swiglu(
+                x64["x"][t:t + 1], x64["w1"][e], x64["w3"][e], x64["w2"][e])[0]
+            _close(capped["y"][t], want, 1e-12, f"token {t} with one dropped slot")
+            n_one += 1
+    assert n_one > 0, "the cap dropped no slot: the pin would test nothing"
+    assert n_both >= 0
+
+
 # --- pre-norm block (RMSNorm before the layer, residual after) ------------------
 
 def pin_rmsnorm_matches_torch(o):

@@ -19,7 +19,7 @@ def test_pin(oracle, pin):
 # 4 normalises over all experts, 5 transposes W_g, 6 transposes W2,
 # 7 swaps the slot weights in the combine, 8 reverses the permute order,
 # 9 takes the 1st-2nd instead of the 2nd-3rd margin.
-MUTANTS = list(range(1, 14))
+MUTANTS = list(range(1, 16))
 
 
 @pytest.mark.parametrize("mutant", MUTANTS)
