@@ -46,6 +46,8 @@ def parse():
                     help="approximate budget of the CPU-oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "stream", "tiled"])
+    ap.add_argument("--capacity-factor", type=float, default=0.0,
+                    help="capacity variant: cap every expert at ceil(cf*T*K/E) rows (0: no cap)")
     ap.add_argument("--block", action="store_true",
                     help="time the pre-norm block instead of the bare layer: RMSNorm of the "
                          "block input before routing, the residual added in the combine")
@@ -189,7 +191,9 @@ def main():
         wsets.append({k: parity.device_array(inp[k], cfg.dtype) for k in ("w1", "w3", "w2")})
     # the staged calls let the down projection leave partial sums for the combine, as
     # the one-call entry point does internally
-    p = moe.problem(T, d, h, E, K, cfg.dtype, "f32", args.path, moe.FLAG_DOWN_PARTIALS)
+    cap = moe.capacity_rows(T, K, E, args.capacity_factor) if args.capacity_factor > 0 else 0
+    p = moe.problem(T, d, h, E, K, cfg.dtype, "f32", args.path, moe.FLAG_DOWN_PARTIALS,
+                    capacity=cap)
     path = "stream" if moe.resolve_path(p) == moe.PATH_STREAM else "tiled"
     parts = moe.down_parts(p)
     if cfg.dtype == "f32":
@@ -376,9 +380,12 @@ def main():
         # once to bf16, so routing is compared with the block's wider near-tie margin)
         tol = dict(tie_margin=1e-2, w_tol=2e-3) if args.block and cfg.dtype == "bf16" else {}
         idx_eval, diff = parity.check_routing(ih, wh, l, idx_r, margin, K, o, **tol)
-        if len(diff):
+        if len(diff) or cap:
+            w_eval = o.set_weights(l, idx_eval)
+            if cap:  # the cap keeps the earliest slots, so the first n tokens decide alone
+                w_eval = o.capped_weights(o.permute_capped(idx_eval, E, cap)[2], w_eval)
             y_ref = o.forward_tokens(toks, xs, inp["w1"], inp["w3"], inp["w2"], idx_eval,
-                                     o.set_weights(l, idx_eval), cfg.dtype)
+                                     w_eval, cfg.dtype)
         y_gpu = parity.host_array(y)[:n].astype(np.float64)
         if args.block:  # compare the MoE part; the residual is added exactly in float32
             y_gpu = y_gpu - mi.to_float64(blk["h"][:n], cfg.dtype)
@@ -401,7 +408,8 @@ def main():
         "data": "synthetic (seeded generator; random-init weights of the layer's shape)",
         "config": {"workload": cfg.name, "T": T, "d": d, "h": h, "E": E, "K": K,
                    "path": path, "down_partial_sums": parts, "weight_copies": copies,
-                   "block": bool(args.block)},
+                   "block": bool(args.block), "capacity": cap,
+                   "capacity_factor": args.capacity_factor},
         "roofline": roof,
         "layer": layer,
         "cpu_baseline": cpu,

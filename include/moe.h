@@ -62,6 +62,14 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 } moe_
 /* Largest T for which MOE_PATH_AUTO picks MOE_PATH_STREAM. */
 #define MOE_STREAM_MAX_T 192
 
+/* moe_problem.capacity (the capacity variant; the pages name the capacity
+ * factor, a cap on the tokens per expert, as general MoE practice: ml-canon
+ * page "52 Mixtral", Questions worth asking). With capacity C > 0 each expert
+ * keeps its C earliest token-slots in (token, k) order; a later slot is dropped:
+ * moe_permute gives it slot_pos -1 and no row, and it adds nothing to its
+ * token's output (the kept weights are not renormalised). A capacity factor cf
+ * corresponds to C = ceil(cf * T * K / E). 0 keeps every slot (Mixtral). */
+
 /* moe_problem.flags bits.
  * MOE_FLAG_DOWN_PARTIALS: the caller lets moe_expert_down / moe_expert_swiglu
  *   split the sum over h into moe_down_parts(p) float32 partial sums, stored one
@@ -80,6 +88,8 @@ typedef struct {
   int32_t out_dtype; /* moe_dtype of y                           */
   int32_t path;      /* moe_path                                 */
   int32_t flags;     /* MOE_FLAG_* bits, 0 for none              */
+  int32_t capacity;  /* rows per expert at most, 0 for no cap    */
+  int32_t reserved;  /* must be 0                                */
 } moe_problem;
 
 /* Human-readable name of a status code. */

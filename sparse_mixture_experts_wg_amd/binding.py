@@ -34,7 +34,8 @@ class Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("h", ctypes.c_int64),
                 ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
     @property
     def S(self) -> int:
@@ -42,8 +43,17 @@ class Problem(ctypes.Structure):
 
 
 def problem(T: int, d: int, h: int, E: int = 8, K: int = 2, dtype: str = "bf16",
-            out_dtype: str = "f32", path: str = "auto", flags: int = 0) -> Problem:
-    return Problem(T, d, h, E, K, _DTYPES[dtype], _DTYPES[out_dtype], _PATHS[path], flags)
+            out_dtype: str = "f32", path: str = "auto", flags: int = 0,
+            capacity: int = 0) -> Problem:
+    return Problem(T, d, h, E, K, _DTYPES[dtype], _DTYPES[out_dtype], _PATHS[path], flags,
+                   capacity, 0)
+
+
+def capacity_rows(T: int, K: int, E: int, capacity_factor: float) -> int:
+    """Rows per expert for a capacity factor: ceil(cf * T * K / E)."""
+    import math
+
+    return int(math.ceil(capacity_factor * T * K / E))
 
 
 def header_functions(path: str = HEADER):

@@ -64,6 +64,8 @@ moe_status check_problem(const moe_problem *p) {
     return fail(MOE_ERR_UNSUPPORTED, "path=%d unknown", p->path);
   if (p->dtype == MOE_F32 && p->path == MOE_PATH_STREAM)
     return fail(MOE_ERR_UNSUPPORTED, "the STREAM path is bf16 only");
+  if (p->capacity < 0) return fail(MOE_ERR_SHAPE, "capacity=%d must be >= 0", p->capacity);
+  if (p->reserved != 0) return fail(MOE_ERR_UNSUPPORTED, "reserved field must be 0");
   if (p->flags & ~MOE_FLAG_DOWN_PARTIALS)
     return fail(MOE_ERR_UNSUPPORTED, "flags=0x%x: unknown bits", unsigned(p->flags));
   // tiled grid: column blocks x (token blocks + E) must fit a 1-D grid
@@ -170,7 +172,7 @@ moe_status do_route(const moe_problem *p, const void *x, const void *w_g, int32_
 moe_status do_permute(const moe_problem *p, const void *x, const int32_t *idx, int32_t *offsets,
                       int32_t *perm, int32_t *slot, void *x_perm, hipStream_t s) {
   const int64_t S = p->T * p->K;
-  CHECK(hip_result(moe::launch_permute_index(idx, S, p->K, p->E, offsets, perm, slot, s),
+  CHECK(hip_result(moe::launch_permute_index(idx, S, p->K, p->E, p->capacity, offsets, perm, slot, s),
                    "permute launch"));
   return hip_result(moe::launch_gather_rows(x, perm, offsets, p->E, S, p->d * esize(p->dtype),
                                             x_perm, s),

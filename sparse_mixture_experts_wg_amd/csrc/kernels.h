@@ -33,7 +33,10 @@ hipError_t launch_route(bool bf16, const void *x, const void *wg, int64_t T, int
                         int32_t *idx, float *w, float *logits, hipStream_t s);
 
 // ---- permute ----------------------------------------------------------------
-hipError_t launch_permute_index(const int32_t *idx, int64_t S, int K, int E, int32_t *offsets,
+// capacity > 0: each expert keeps its `capacity` earliest slots, later ones get
+// slot_pos -1 and no row.
+hipError_t launch_permute_index(const int32_t *idx, int64_t S, int K, int E, int capacity,
+                                int32_t *offsets,
                                 int32_t *perm_token, int32_t *slot_pos, hipStream_t s);
 hipError_t launch_gather_rows(const void *x, const int32_t *perm_token, const int32_t *offsets,
                               int E, int64_t S, int64_t row_bytes, void *x_perm, hipStream_t s);

@@ -12,6 +12,9 @@
 // and a second pass over the same range assigns rows in slot order. The result
 // is the stable order (ascending s = t*K + k within an expert) with no atomics.
 // The slot index arrays are small (S int32), so one CU suffices.
+// With a capacity C (the capacity variant) a slot whose rank within its expert
+// is C or more is dropped (slot_pos -1, no row) and the offsets count the kept
+// rows min(n_e, C) only.
 //
 // gather_rows: one wavefront per sorted row copies x[perm_token[r]] with 16-byte
 // loads/stores.
@@ -24,7 +27,8 @@ constexpr int kThreads = 1024;
 constexpr int kWavesPerBlock = kThreads / 64;
 
 __global__ __launch_bounds__(kThreads) void permute_index_kernel(
-    const int32_t *__restrict__ idx, int64_t S, int K, int E, int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ idx, int64_t S, int K, int E, int capacity,
+    int32_t *__restrict__ offsets,
     int32_t *__restrict__ perm_token, int32_t *__restrict__ slot_pos) {
   __shared__ int32_t wave_tot[kWavesPerBlock][8];
   __shared__ int32_t wave_pre[kWavesPerBlock][8];
@@ -71,28 +75,30 @@ __global__ __launch_bounds__(kThreads) void permute_index_kernel(
     wave_tot[0][tid] = run;  // expert total (wave_tot[0] is no longer needed)
   }
   __syncthreads();
+  const int cap = capacity > 0 ? capacity : 0x7FFFFFFF;
   if (tid == 0) {
     int run = 0;
     expert_off[0] = 0;
     for (int e = 0; e < 8; ++e) {
-      run += (e < E) ? wave_tot[0][e] : 0;
+      run += (e < E) ? min(wave_tot[0][e], cap) : 0;
       expert_off[e + 1] = run;
     }
     for (int e = 0; e <= E; ++e) offsets[e] = expert_off[e];
   }
   __syncthreads();
 
-  int pos[8];
+  // rank of this thread's first slot of each expert among that expert's slots
+  int rank[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pos[e] = expert_off[e] + wave_pre[wave][e] + incl[e] - cnt[e];
+  for (int e = 0; e < 8; ++e) rank[e] = wave_pre[wave][e] + incl[e] - cnt[e];
   for (int64_t s = s0; s < s1; ++s) {
     const int e = idx[s];
     int p = -1;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if (q == e && q < E) {
-        p = pos[q];
-        pos[q] = p + 1;
+        if (rank[q] < cap) p = expert_off[q] + rank[q];
+        rank[q] += 1;
       }
     }
     slot_pos[s] = p;
@@ -116,10 +122,11 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restric
 
 }  // namespace
 
-hipError_t launch_permute_index(const int32_t *idx, int64_t S, int K, int E, int32_t *offsets,
-                                int32_t *perm_token, int32_t *slot_pos, hipStream_t s) {
-  hipLaunchKernelGGL(permute_index_kernel, dim3(1), dim3(kThreads), 0, s, idx, S, K, E, offsets,
-                     perm_token, slot_pos);
+hipError_t launch_permute_index(const int32_t *idx, int64_t S, int K, int E, int capacity,
+                                int32_t *offsets, int32_t *perm_token, int32_t *slot_pos,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(permute_index_kernel, dim3(1), dim3(kThreads), 0, s, idx, S, K, E, capacity,
+                     offsets, perm_token, slot_pos);
   return hipGetLastError();
 }
 

@@ -80,6 +80,17 @@ def test_path_resolution():
     assert moe.resolve_path(_p(dtype="f32")) == binding.PATH_TILED
 
 
+def test_capacity_field():
+    assert moe.resolve_path(_p(capacity=5)) == binding.PATH_STREAM
+    assert moe.resolve_path(_p(capacity=-1)) == -binding.ERR_SHAPE
+    p = _p()
+    p.reserved = 3
+    assert moe.resolve_path(p) == -binding.ERR_UNSUPPORTED
+    assert moe.capacity_rows(4096, 2, 8, 1.0) == 1024
+    assert moe.capacity_rows(100, 2, 8, 1.25) == 32  # ceil(31.25)
+    assert ctypes.sizeof(binding.Problem) == 56
+
+
 def test_down_parts():
     """Partial sums only when asked for, on the tiled bf16 path, with h % 256 == 0 and
     few down-projection row tiles (fewer than 4 per compute unit of MI355X)."""

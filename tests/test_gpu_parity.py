@@ -255,6 +255,83 @@ def test_permute_all_to_one_and_dropped_ids(moe, oracle):
     assert np.array_equal(parity.host_array(xp)[:n], x[order // K])
 
 
+# ---- capacity variant ---------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,K,cap", [(700, 8, 2, 1), (700, 8, 2, 50), (700, 8, 2, 175),
+                                       (700, 8, 2, 100000), (333, 3, 1, 40), (64, 8, 2, 3)])
+def test_permute_capacity_exact(moe, oracle, T, E, K, cap):
+    idx = mi.make_routing(T, E, K, seed=T + cap)
+    idx[: T // 2, 0] = 0  # crowd expert 0 so that the cap bites
+    if K > 1:
+        idx[: T // 2, 1] = np.where(idx[: T // 2, 1] == 0, 1, idx[: T // 2, 1])
+    d = 128
+    x = mi.make_x(mi.Config("pc", T=T, d=d, h=128, E=E, K=K), seed=3)
+    p = moe.problem(T, d, 128, E, K, "bf16", capacity=cap)
+    off, perm, slot, xp = moe.permute(p, parity.device_array(x, "bf16"),
+                                      parity.device_array(idx, "i32"))
+    torch.cuda.synchronize()
+    off_r, perm_r, slot_r = oracle.permute_capped(idx, E, cap)
+    n = int(off_r[-1])
+    assert np.array_equal(parity.host_array(off), off_r)
+    assert np.array_equal(parity.host_array(slot), slot_r)
+    assert np.array_equal(parity.host_array(perm)[:n], perm_r[:n])
+    assert np.array_equal(parity.host_array(xp)[:n], x[perm_r[:n]])
+
+
+def _capacity_ref(oracle, inp, cfg, cap, idx_gpu, w_gpu, tokens):
+    """Oracle layer under the cap, with rule R: near-tie tokens keep the GPU's valid set,
+    and the cap is applied to that routing (a different set for an early token changes
+    which later slots an expert still has room for)."""
+    l, idx, w, margin = oracle.route(inp["x"], inp["w_g"], cfg.K, cfg.dtype)
+    idx_eval, diff = parity.check_routing(idx_gpu, w_gpu, l, idx, margin, cfg.K, oracle)
+    _, _, slot_ref = oracle.permute_capped(idx_eval, cfg.E, cap)
+    w_cap = oracle.capped_weights(slot_ref, oracle.set_weights(l, idx_eval))
+    y_ref = oracle.forward_tokens(tokens, inp["x"], inp["w1"], inp["w3"], inp["w2"], idx_eval,
+                                  w_cap, cfg.dtype)
+    return y_ref, slot_ref
+
+
+@pytest.mark.parametrize("name,cfg,cf,path", [
+    ("tiled_cf1", mi.Config("c1", T=600, d=256, h=384, wg_std="fan_in_d", zipf_bias=True), 1.0,
+     "auto"),
+    ("stream_cf1", mi.Config("c2", T=96, d=256, h=256, wg_std="fan_in_d", zipf_bias=True), 1.0,
+     "auto"),
+    ("tiled_cf0.5", mi.Config("c3", T=400, d=128, h=256, wg_std="fan_in_d"), 0.5, "tiled"),
+], ids=["tiled_cf1", "stream_cf1", "tiled_cf0.5"])
+def test_forward_capacity(moe, oracle, name, cfg, cf, path):
+    """The capacity variant: every expert keeps its earliest C = ceil(cf T K / E) slots;
+    the output matches the oracle's capped layer and the dropped slots are the same."""
+    inp = mi.make_inputs(cfg, seed=15)
+    cap = moe.capacity_rows(cfg.T, cfg.K, cfg.E, cf)
+    p = moe.problem(cfg.T, cfg.d, cfg.h, cfg.E, cfg.K, cfg.dtype, "f32", path,
+                    moe.FLAG_DOWN_PARTIALS, capacity=cap)  # partial sums as moe_forward uses
+    dev = parity.upload_inputs(inp, cfg.dtype)
+    idx, w, _ = moe.route(p, dev["x"], dev["w_g"])
+    offsets, perm, slot, x_perm = moe.permute(p, dev["x"], idx)
+    y_staged = moe.combine(p, moe.expert_swiglu(p, x_perm, offsets, dev["w1"], dev["w3"],
+                                                dev["w2"]), slot, w)
+    y = moe.forward(p, dev["x"], dev["w_g"], dev["w1"], dev["w3"], dev["w2"])
+    torch.cuda.synchronize()
+    yh = parity.host_array(y).astype(np.float64)
+    assert np.array_equal(parity.host_array(y_staged).astype(np.float64), yh)
+    ih, wh, sh = parity.host_array(idx), parity.host_array(w), parity.host_array(slot)
+    y_ref, slot_ref = _capacity_ref(oracle, inp, cfg, cap, ih, wh, np.arange(cfg.T))
+    assert np.array_equal(sh < 0, slot_ref < 0), "dropped slots differ"
+    assert np.sum(sh < 0) > 0, "the cap dropped nothing: the test would test nothing"
+    parity.check_output(yh, y_ref, cfg.dtype, f"capacity {name}")
+
+
+def test_capacity_at_least_T_changes_nothing(moe):
+    cfg = mi.Config("c4", T=300, d=256, h=384, wg_std="fan_in_d")
+    inp = mi.make_inputs(cfg, seed=16)
+    y0 = _run_forward(moe, cfg, inp, "tiled")[0]
+    p = moe.problem(cfg.T, cfg.d, cfg.h, cfg.E, cfg.K, "bf16", "f32", "tiled", capacity=cfg.T)
+    dev = parity.upload_inputs(inp, "bf16")
+    y = moe.forward(p, dev["x"], dev["w_g"], dev["w1"], dev["w3"], dev["w2"])
+    torch.cuda.synchronize()
+    assert np.array_equal(parity.host_array(y).astype(np.float64), y0)
+
+
 def _segments(counts):
     return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
 
