@@ -306,10 +306,11 @@ def main():
     es = 2 if cfg.dtype == "bf16" else 4
     hit = int(np.sum(counts > 0))
     gu_ms = gu_ms_live
-    gu_bytes = hit * 2 * h * d * es + S * d * es + S * h * es
-    gu_flop = 2.0 * S * d * 2 * h
+    S_rows = int(counts.sum())  # rows the experts run: S, or fewer under a capacity cap
+    gu_bytes = hit * 2 * h * d * es + S_rows * d * es + S_rows * h * es
+    gu_flop = 2.0 * S_rows * d * 2 * h
     layer_bytes = hit * 3 * h * d * es + d * E * es + T * d * es + T * d * 4
-    layer_flop = 2.0 * S * 3 * d * h + 2.0 * T * d * E
+    layer_flop = 2.0 * S_rows * 3 * d * h + 2.0 * T * d * E
     kernel = {"stream": "stream_gate_up", "tiled": "tiled_gate_up", "f32": "f32_gate_up"}[path]
     sha = source_hash(kernel_files(path)) if path != "f32" else None
     traffic_rec = load_traffic(cfg.name, kernel, sha) if sha else None
