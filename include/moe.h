@@ -99,7 +99,7 @@ const char *moe_status_string(int status);
 const char *moe_last_error(void);
 
 /* Number of float32 partial sums per row that moe_expert_down and
- * moe_expert_swiglu write into o_perm for `p` (1, or 2 when p->flags has
+ * moe_expert_swiglu write into o_perm for `p` (1, or 2 or 4 when p->flags has
  * MOE_FLAG_DOWN_PARTIALS and the down projection is split), or -status if `p`
  * is invalid. o_perm then holds parts * S * d floats. */
 int moe_down_parts(const moe_problem *p);

@@ -103,18 +103,46 @@ moe_status hip_result(hipError_t e, const char *what) {
   return MOE_OK;
 }
 
-// Partial sums of the down projection (see MOE_FLAG_DOWN_PARTIALS): the tiled
-// kernel splits the h sum in two when the row tiles of the down projection would
-// fill the 256 compute units fewer than 4 times over (with one tile per compute
-// unit at a time, the last, partly filled round then costs less).
+// Token tile of the tiled bf16 kernels: 384 tokens once an expert holds that
+// many rows on average (fewer bytes from L2 per flop), else 256 (less padding).
+// Measured on MI355X at d = 4096, h = 14336: the gate-up projection gains from
+// 384 at >= 1024 rows per expert, the down projection from >= 256.
 constexpr int64_t kCUs = 256;
 
+int64_t rows_per_expert(const moe_problem *p) { return (p->T * p->K + p->E - 1) / p->E; }
+
+int gate_up_tile(const moe_problem *p) { return rows_per_expert(p) >= 1024 ? 384 : 256; }
+int down_tile(const moe_problem *p) { return rows_per_expert(p) >= 256 ? 384 : 256; }
+
+// Partial sums of the down projection (see MOE_FLAG_DOWN_PARTIALS): the tiled
+// kernel can cut the sum over h into 2 or 4 parts, each a workgroup of its own,
+// so that the last, partly filled round of workgroups (one per compute unit at
+// a time) costs less. Estimated cost of p parts, in k-blocks of one round:
+// rounds(p) * (k-blocks per part + 8 for a tile's set-up and epilogue), plus
+// the extra float32 partial sums written and read again (about 13.5 MB per
+// unit at the measured ~5 TB/s). Tiles are estimated from an even split of the
+// rows over the experts.
 int down_parts(const moe_problem *p) {
   if (!(p->flags & MOE_FLAG_DOWN_PARTIALS) || p->dtype != MOE_BF16) return 1;
-  if (resolve(p) != MOE_PATH_TILED || p->h % 256) return 1;
+  if (resolve(p) != MOE_PATH_TILED) return 1;
+  const int64_t bt = down_tile(p);
   const int64_t S = p->T * p->K;
-  const int64_t tiles = (p->d / 256 + (p->d % 256 != 0)) * ((S + 255) / 256 + p->E);
-  return tiles < 4 * kCUs ? 2 : 1;
+  const int64_t tiles = ((p->d + 255) / 256) * p->E * ((rows_per_expert(p) + bt - 1) / bt);
+  const int64_t nk = p->h / 64;
+  const double unit_bytes = 13.5e6 * double(bt) / 384.0;
+  int best = 1;
+  double best_cost = 0.0;
+  for (int parts = 1; parts <= 4; parts *= 2) {
+    if (nk % (2 * parts)) break;  // each part needs an even count of 64-wide k-blocks
+    const int64_t rounds = (tiles * parts + kCUs - 1) / kCUs;
+    const double cost = double(rounds) * double(nk / parts + 8) +
+                        double(parts - 1) * double(S) * double(p->d) * 8.0 / unit_bytes;
+    if (parts == 1 || cost < best_cost) {
+      best = parts;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 struct ForwardLayout {
@@ -191,7 +219,8 @@ moe_status do_gate_up(const moe_problem *p, const void *x_perm, const int32_t *o
     e = moe::launch_stream_gate_up(x_perm, offsets, w1, w3, act, p->E, int(p->d), int(p->h), p->T,
                                    S, s);
   else
-    e = moe::launch_tiled_gate_up(x_perm, offsets, w1, w3, act, p->E, S, int(p->d), int(p->h), s);
+    e = moe::launch_tiled_gate_up(x_perm, offsets, w1, w3, act, p->E, S, int(p->d), int(p->h),
+                                  gate_up_tile(p), s);
   return hip_result(e, "gate-up launch");
 }
 
@@ -207,7 +236,8 @@ moe_status do_down(const moe_problem *p, const void *act, const int32_t *offsets
     e = moe::launch_stream_down(act, offsets, w2, o_perm, p->E, int(p->d), int(p->h), p->T, S,
                                 s);
   else
-    e = moe::launch_tiled_down(act, offsets, w2, o_perm, p->E, S, int(p->d), int(p->h), parts, s);
+    e = moe::launch_tiled_down(act, offsets, w2, o_perm, p->E, S, int(p->d), int(p->h),
+                               down_tile(p), parts, s);
   return hip_result(e, "down launch");
 }
 

@@ -7,15 +7,19 @@
 // the sparse-matmul kernels the pages cite are prior art, this is a plain
 // grouped GEMM over the per-expert segments).
 //
-// Tile: 256 weight rows (MFMA M side) x 256 tokens (MFMA N side) x 64 k.
-//  * 8 wavefronts (2 per SIMD) in a 2 x 4 grid; each owns 128 weight rows x 64
-//    tokens as 4 x 2 accumulators of v_mfma_f32_32x32x16_bf16. Two wavefronts
-//    per SIMD keep the matrix pipe fed while the other waits on LDS or a barrier
-//    (one wavefront per SIMD tops out near 80% of the matrix peak on gfx950).
+// Tile: 256 weight rows (MFMA M side) x BT tokens (MFMA N side, BT = 256 or
+// 384) x 64 k.
+//  * 8 wavefronts (2 per SIMD) in a 2 x 4 grid; each owns 128 weight rows x
+//    BT/4 tokens as 4 x BT/128 accumulators of v_mfma_f32_32x32x16_bf16. Two
+//    wavefronts per SIMD keep the matrix pipe fed while the other waits on LDS
+//    or a barrier. BT = 384 is the largest tile whose accumulators (192
+//    registers) fit two wavefronts per SIMD; it moves 17% fewer bytes from L2
+//    per flop than BT = 256, which it replaces once experts hold >= 256 rows
+//    on average (with fewer rows the wider tile only adds padding).
 //  * Global memory goes straight to LDS (global_load_lds_dwordx4: a wavefront
 //    instruction fills one contiguous kilobyte, lane L the bytes [16L, 16L+16)),
-//    two stages of 64 KiB; the k-block after the current one is in flight while
-//    the current one is multiplied; one barrier per k-block.
+//    two stages (64 or 80 KiB each); the k-block after the current one is in
+//    flight while the current one is multiplied; one barrier per k-block.
 //  * LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by
 //    (r ^ r >> 3) & 7 of the row's position in its 32-row group, so both the
 //    DMA writes and the fragment reads of 8 or 16 consecutive rows hit distinct
@@ -30,9 +34,9 @@
 //    round-robin) owns one contiguous range of tiles and its own L2 sees the
 //    reuse. Token rows past an expert's end are clamped duplicates whose results
 //    are never stored.
-//  * Down with few row tiles can split the sum over h in two: each half is a
-//    tile of its own writing float32 partial sums that the combine step adds
-//    in a fixed order, so that the last round of tiles fills the GPU.
+//  * Down can split the sum over h into `ksplit` parts: each part is a tile of
+//    its own writing float32 partial sums that the combine step adds in a fixed
+//    order, so that the last round of tiles fills the GPU.
 #include "kernels.h"
 
 namespace moe {
@@ -47,14 +51,15 @@ constexpr int kWaitVm0 = 0x0F70;
 // Physical 16-byte chunk = logical chunk ^ swz(row); depends on row & 31 only.
 __device__ __forceinline__ int swz(int r) { return ((r & 31) ^ ((r & 31) >> 3)) & 7; }
 
-template <bool GATEUP>
+template <bool GATEUP, int BT>
 __global__ __launch_bounds__(512) void tiled_kernel(const uint16_t *__restrict__ X,
                                                      const int32_t *__restrict__ offsets, int E,
                                                      const uint16_t *__restrict__ Wa,
                                                      const uint16_t *__restrict__ Wb,
                                                      void *__restrict__ out, int N, int K,
                                                      int ksplit, int64_t part_stride) {
-  constexpr int BT = 256;
+  constexpr int NT = BT / 128;        // 32-token accumulator columns per wavefront
+  constexpr int XI = BT / 64;         // token-row DMA instructions per wavefront
   constexpr int kCols = GATEUP ? 128 : 256;
   const int ct = (N + kCols - 1) / kCols;
   int total = 0;
@@ -82,56 +87,69 @@ __global__ __launch_bounds__(512) void tiled_kernel(const uint16_t *__restrict__
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // (BT = 384 keeps wave-uniform values in scalar registers: the vector
+  // registers are all but taken by its accumulators)
+  const int wave = BT == 384 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int wr = wave >> 2, wc = wave & 3;
 
   __shared__ __attribute__((aligned(1024))) uint16_t sW0[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
-  __shared__ __attribute__((aligned(1024))) uint16_t sX0[256 * 64];
-  __shared__ __attribute__((aligned(1024))) uint16_t sX1[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX0[BT * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX1[BT * 64];
 
-  // ---- DMA assignment: wave w fills rows [32w, 32w+32) of both tiles, 8 rows per
-  // instruction; lane p writes LDS bytes [16p, 16p+16) of the instruction's
-  // kilobyte: row 8i + p/8, physical chunk p%8 = logical chunk ^ swz(row).
+  // ---- DMA assignment: wave w fills weight rows [32w, 32w+32) and token rows
+  // [w*BT/8, (w+1)*BT/8), 8 rows per instruction; lane p writes LDS bytes
+  // [16p, 16p+16) of the instruction's kilobyte: row 8i + p/8, physical chunk
+  // p%8 = logical chunk ^ swz(row). Instruction i of a share starting at row s
+  // covers position 8 * ((s/8 + i) & 3) + p/8 of a 32-row group.
   const size_t mat_elems = size_t(N) * K;
   const uint16_t *wmat = Wa + size_t(e) * mat_elems;
   if (GATEUP && ((wave >> 1) & 1)) wmat = Wb + size_t(e) * mat_elems;
   const uint16_t *x_t = X + size_t(row0 + m0) * K;
-  uint32_t wofs[4], xofs[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 32 + i * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    int wrow;
-    if constexpr (GATEUP) wrow = c0 + ((r >> 7) << 6) + (r & 63);
-    else wrow = min(c0 + r, N - 1);
-    wofs[i] = uint32_t(wrow) * uint32_t(K) + c * 8;
-    xofs[i] = uint32_t(min(r, ne - 1 - m0)) * uint32_t(K) + c * 8;
-  }
+  const int wrow0 = GATEUP ? c0 + (wave >> 2) * 64 + (wave & 1) * 32 : c0 + wave * 32;
+  const int xlim = ne - 1 - m0;
   const int dma_row = wave * 32;
+  const int dma_xrow = wave * (BT / 8);
+  // BT = 256: the per-lane DMA offsets are computed once (registers to spare)
+  uint32_t wofs[4], xofs[4];
+  if constexpr (BT == 256) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 32 + i * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      int wrow;
+      if constexpr (GATEUP) wrow = c0 + ((r >> 7) << 6) + (r & 63);
+      else wrow = min(c0 + r, N - 1);
+      wofs[i] = uint32_t(wrow) * uint32_t(K) + c * 8;
+      xofs[i] = uint32_t(min(r, xlim)) * uint32_t(K) + c * 8;
+    }
+  }
 
   // ---- fragment read addresses (bytes): row (lane & 31) of a 32-row group,
   // logical chunk kk*2 + (lane >> 5)
   const int g = (lane >> 5) ^ swz(lane & 31);
-  uint32_t offk[4];
+  uint32_t offk0[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) offk[kk] = uint32_t(((kk * 2) ^ g) * 16);
+  for (int kk = 0; kk < 4; ++kk) offk0[kk] = uint32_t(((kk * 2) ^ g) * 16);
   const uint32_t baseA = uint32_t((wr * 128 + (lane & 31)) * 128);
-  const uint32_t baseB = uint32_t((wc * 64 + (lane & 31)) * 128);
+  const uint32_t baseB = uint32_t((wc * (BT / 4) + (lane & 31)) * 128);
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][NT];
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[f][t][i] = 0.f;
 
   const int nk = K / 64 / ksplit;  // k-blocks of this part (an even count)
   const int kb0 = ks * nk;
 
+  // BT = 384: the DMA and fragment addresses are recomputed from opaque
+  // copies of the lane values at each use, so that they hold no registers
+  // across the main loop (its accumulators leave almost none).
 #define DMA(SW, SX, KB)                                                                    \
-  {                                                                                        \
+  if constexpr (BT == 256) {                                                               \
     const uint32_t k0 = uint32_t((kb0 + min(KB, nk - 1)) * 64);                            \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                        \
       __builtin_amdgcn_global_load_lds(wmat + wofs[i] + k0,                                \
@@ -139,32 +157,87 @@ __global__ __launch_bounds__(512) void tiled_kernel(const uint16_t *__restrict__
       __builtin_amdgcn_global_load_lds(x_t + xofs[i] + k0,                                 \
                                        (lds_void *)(SX + (dma_row + i * 8) * 64), 16, 0, 0); \
     }                                                                                      \
+  } else {                                                                                 \
+    const uint32_t k0 = uint32_t((kb0 + min(KB, nk - 1)) * 64);                            \
+    int ln = lane;                                                                         \
+    asm volatile("" : "+v"(ln));                                                           \
+    const int lr = ln >> 3, lc = ln & 7;                                                   \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                        \
+      const int wrow = GATEUP ? wrow0 + 8 * i + lr : min(wrow0 + 8 * i + lr, N - 1);      \
+      const uint32_t o = uint32_t(wrow) * uint32_t(K) + ((lc ^ lr ^ i) << 3) + k0;         \
+      __builtin_amdgcn_global_load_lds(wmat + o, (lds_void *)(SW + (dma_row + i * 8) * 64), \
+                                       16, 0, 0);                                          \
+    }                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < XI; ++i) {                                       \
+      const int xrow = min(dma_xrow + 8 * i + lr, xlim);                                   \
+      const int q = (dma_xrow / 8 + i) & 3;                                                \
+      const uint32_t o = uint32_t(xrow) * uint32_t(K) + ((lc ^ lr ^ q) << 3) + k0;         \
+      __builtin_amdgcn_global_load_lds(x_t + o, (lds_void *)(SX + (dma_xrow + i * 8) * 64), \
+                                       16, 0, 0);                                          \
+    }                                                                                      \
   }
+  // NT = 2: both fragment sets double-buffered, the next kk's six reads issued
+  // ahead of the current kk's eight MFMAs. NT = 3 (no registers for that): the
+  // token fragments double-buffered, each weight fragment reloaded for the next
+  // kk as soon as its three MFMAs are issued.
 #define COMPUTE(SW, SX)                                                                    \
   {                                                                                        \
     const char *pa = reinterpret_cast<const char *>(SW) + baseA;                           \
     const char *pb = reinterpret_cast<const char *>(SX) + baseB;                           \
-    bf16x8 fa[2][4], fb[2][2];                                                             \
-    _Pragma("unroll") for (int f = 0; f < 4; ++f)                                          \
-      fa[0][f] = *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[0]);               \
-    _Pragma("unroll") for (int t = 0; t < 2; ++t)                                          \
-      fb[0][t] = *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[0]);               \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                     \
-      const int cur = kk & 1;                                                              \
-      if (kk + 1 < 4) {                                                                    \
-        _Pragma("unroll") for (int f = 0; f < 4; ++f) fa[cur ^ 1][f] =                     \
-            *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[kk + 1]);               \
-        _Pragma("unroll") for (int t = 0; t < 2; ++t) fb[cur ^ 1][t] =                     \
-            *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[kk + 1]);               \
-      }                                                                                    \
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);                                   \
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);                                   \
+    if constexpr (NT == 2) {                                                               \
+      const uint32_t *offk = offk0;                                                        \
+      bf16x8 fa[2][4], fb[2][2];                                                           \
+      _Pragma("unroll") for (int f = 0; f < 4; ++f)                                        \
+        fa[0][f] = *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[0]);             \
       _Pragma("unroll") for (int t = 0; t < 2; ++t)                                        \
-        _Pragma("unroll") for (int f = 0; f < 4; ++f)                                      \
-          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][f], fb[cur][t],      \
-                                                              acc[f][t], 0, 0, 0);         \
+        fb[0][t] = *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[0]);             \
       __builtin_amdgcn_sched_barrier(0);                                                   \
+      _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                   \
+        const int cur = kk & 1;                                                            \
+        if (kk + 1 < 4) {                                                                  \
+          _Pragma("unroll") for (int f = 0; f < 4; ++f) fa[cur ^ 1][f] =                   \
+              *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[kk + 1]);             \
+          _Pragma("unroll") for (int t = 0; t < 2; ++t) fb[cur ^ 1][t] =                   \
+              *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[kk + 1]);             \
+        }                                                                                  \
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);                                 \
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);                                 \
+        _Pragma("unroll") for (int t = 0; t < 2; ++t)                                      \
+          _Pragma("unroll") for (int f = 0; f < 4; ++f)                                    \
+            acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][f], fb[cur][t],    \
+                                                                acc[f][t], 0, 0, 0);       \
+        __builtin_amdgcn_sched_barrier(0);                                                 \
+      }                                                                                    \
+    } else {                                                                               \
+      int gg = g;                                                                          \
+      asm volatile("" : "+v"(gg));                                                         \
+      uint32_t offk[4];                                                                    \
+      _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) offk[kk] = uint32_t(((kk * 2) ^ gg) * 16); \
+      bf16x8 fa[4], fb[2][NT];                                                             \
+      _Pragma("unroll") for (int t = 0; t < NT; ++t)                                       \
+        fb[0][t] = *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[0]);             \
+      _Pragma("unroll") for (int f = 0; f < 4; ++f)                                        \
+        fa[f] = *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[0]);                \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+      _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                   \
+        const int cur = kk & 1;                                                            \
+        if (kk + 1 < 4) {                                                                  \
+          _Pragma("unroll") for (int t = 0; t < NT; ++t) fb[cur ^ 1][t] =                  \
+              *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[kk + 1]);             \
+          __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);                              \
+        }                                                                                  \
+        _Pragma("unroll") for (int f = 0; f < 4; ++f) {                                    \
+          _Pragma("unroll") for (int t = 0; t < NT; ++t)                                   \
+            acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f], fb[cur][t],         \
+                                                                acc[f][t], 0, 0, 0);       \
+          __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);                              \
+          if (kk + 1 < 4) {                                                                \
+            fa[f] = *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[kk + 1]);       \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             \
+          }                                                                                \
+        }                                                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                 \
+      }                                                                                    \
     }                                                                                      \
   }
 
@@ -188,8 +261,8 @@ __global__ __launch_bounds__(512) void tiled_kernel(const uint16_t *__restrict__
   // i = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4) of each 32x32 fragment.
   const int ih = 4 * (lane >> 5);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int tok = m0 + wc * 64 + t * 32 + (lane & 31);
+  for (int t = 0; t < NT; ++t) {
+    const int tok = m0 + wc * (BT / 4) + t * 32 + (lane & 31);
     if (tok >= ne) continue;
     const size_t orow = size_t(row0 + tok) * N + size_t(ks) * size_t(part_stride);
     if constexpr (GATEUP) {
@@ -225,31 +298,41 @@ __global__ __launch_bounds__(512) void tiled_kernel(const uint16_t *__restrict__
 }
 
 // Upper bound of the tile count for any split of S rows over E experts.
-inline unsigned tiled_grid(int64_t S, int E, int N, int cols, int ksplit) {
+inline unsigned tiled_grid(int64_t S, int E, int N, int cols, int bt, int ksplit) {
   const int64_t ct = (N + cols - 1) / cols;
-  const int64_t tiles = ksplit * ct * ((S + 255) / 256 + E);
+  const int64_t tiles = ksplit * ct * ((S + bt - 1) / bt + E);
   return unsigned((tiles + kXCD - 1) / kXCD * kXCD);
+}
+
+template <bool GATEUP, int BT>
+void launch_t(const void *x, const int32_t *offsets, const void *wa, const void *wb, void *out,
+              int E, int64_t S, int N, int K, int ksplit, int64_t part_stride, hipStream_t s) {
+  hipLaunchKernelGGL((tiled_kernel<GATEUP, BT>),
+                     dim3(tiled_grid(S, E, N, GATEUP ? 128 : 256, BT, ksplit)), dim3(512), 0, s,
+                     static_cast<const uint16_t *>(x), offsets, E,
+                     static_cast<const uint16_t *>(wa), static_cast<const uint16_t *>(wb), out, N,
+                     K, ksplit, part_stride);
 }
 
 }  // namespace
 
 hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
-                                 const void *w3, void *act, int E, int64_t S, int d, int h,
-                                 hipStream_t s) {
-  hipLaunchKernelGGL((tiled_kernel<true>), dim3(tiled_grid(S, E, h, 128, 1)), dim3(512), 0, s,
-                     static_cast<const uint16_t *>(x_perm), offsets, E,
-                     static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3), act, h, d,
-                     1, int64_t(0));
+                                const void *w3, void *act, int E, int64_t S, int d, int h,
+                                int bt, hipStream_t s) {
+  if (bt == 384)
+    launch_t<true, 384>(x_perm, offsets, w1, w3, act, E, S, h, d, 1, 0, s);
+  else
+    launch_t<true, 256>(x_perm, offsets, w1, w3, act, E, S, h, d, 1, 0, s);
   return hipGetLastError();
 }
 
 hipError_t launch_tiled_down(const void *act, const int32_t *offsets, const void *w2,
-                              float *o_perm, int E, int64_t S, int d, int h, int parts,
-                              hipStream_t s) {
-  hipLaunchKernelGGL((tiled_kernel<false>), dim3(tiled_grid(S, E, d, 256, parts)), dim3(512), 0, s,
-                     static_cast<const uint16_t *>(act), offsets, E,
-                     static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(nullptr),
-                     static_cast<void *>(o_perm), d, h, parts, S * d);
+                             float *o_perm, int E, int64_t S, int d, int h, int bt, int parts,
+                             hipStream_t s) {
+  if (bt == 384)
+    launch_t<false, 384>(act, offsets, w2, nullptr, o_perm, E, S, d, h, parts, S * d, s);
+  else
+    launch_t<false, 256>(act, offsets, w2, nullptr, o_perm, E, S, d, h, parts, S * d, s);
   return hipGetLastError();
 }
 

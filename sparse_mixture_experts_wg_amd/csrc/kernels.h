@@ -52,14 +52,14 @@ hipError_t launch_stream_gate_up(const void *x_perm, const int32_t *offsets, con
 hipError_t launch_stream_down(const void *act, const int32_t *offsets, const void *w2,
                               float *o_perm, int E, int d, int h, int64_t rows_hint,
                               int64_t rows_bound, hipStream_t s);
-// TILED path (bf16 matrix cores).
+// TILED path (bf16 matrix cores); bt: token tile, 256 or 384.
 hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
                                 const void *w3, void *act, int E, int64_t S, int d, int h,
-                                hipStream_t s);
-// parts (1 or 2; 2 needs h % 256 == 0): partial sums over h, part q at
-// o_perm + q * S * d.
+                                int bt, hipStream_t s);
+// parts (1, 2 or 4; needs h % (128 * parts) == 0): partial sums over h, part q
+// at o_perm + q * S * d.
 hipError_t launch_tiled_down(const void *act, const int32_t *offsets, const void *w2,
-                             float *o_perm, int E, int64_t S, int d, int h, int parts,
+                             float *o_perm, int E, int64_t S, int d, int h, int bt, int parts,
                              hipStream_t s);
 // float32 problems.
 hipError_t launch_f32_gate_up(const float *x_perm, const int32_t *offsets, const float *w1,

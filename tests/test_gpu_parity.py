@@ -337,36 +337,43 @@ def _segments(counts):
 
 
 EXPERT_CASES = [
-    # name, path, T, d, h, counts per expert, flags
-    ("stream_mixed", "stream", 64, 512, 640, [0, 5, 64, 1, 0, 33, 17, 2], 0),
-    ("stream_small", "stream", 32, 256, 384, [3, 0, 0, 16, 32, 1, 0, 4], 0),
-    ("stream_over64", "stream", 150, 256, 256, [150, 0, 70, 0, 0, 0, 0, 1], 0),
+    # name, path, T, d, h, counts per expert, flags, partial sums expected
+    ("stream_mixed", "stream", 64, 512, 640, [0, 5, 64, 1, 0, 33, 17, 2], 0, 1),
+    ("stream_small", "stream", 32, 256, 384, [3, 0, 0, 16, 32, 1, 0, 4], 0, 1),
+    ("stream_over64", "stream", 150, 256, 256, [150, 0, 70, 0, 0, 0, 0, 1], 0, 1),
     # segments longer than T are allowed by the offsets contract (up to S = T*K)
-    ("stream_segment_over_T", "stream", 40, 256, 256, [70, 0, 0, 0, 0, 0, 0, 10], 0),
-    ("stream_T16_segment_30", "stream", 16, 256, 256, [30, 0, 2, 0, 0, 0, 0, 0], 0),
-    ("tiled_mixed", "tiled", 1500, 256, 640, [0, 300, 1, 256, 513, 0, 77, 1000], 0),
-    ("tiled_one", "tiled", 40, 128, 128, [0, 0, 0, 0, 0, 0, 0, 1], 0),
-    ("tiled_d384", "tiled", 600, 384, 256, [200, 57, 0, 0, 300, 0, 1, 9], 0),
-    # down projection split into two partial sums over h
-    ("tiled_partials", "tiled", 600, 384, 512, [200, 57, 0, 0, 300, 0, 1, 9], 1),
-    ("tiled_partials_h1024", "tiled", 300, 256, 1024, [0, 256, 1, 0, 300, 0, 0, 40], 1),
+    ("stream_segment_over_T", "stream", 40, 256, 256, [70, 0, 0, 0, 0, 0, 0, 10], 0, 1),
+    ("stream_T16_segment_30", "stream", 16, 256, 256, [30, 0, 2, 0, 0, 0, 0, 0], 0, 1),
+    ("tiled_mixed", "tiled", 1500, 256, 640, [0, 300, 1, 256, 513, 0, 77, 1000], 0, 1),
+    ("tiled_one", "tiled", 40, 128, 128, [0, 0, 0, 0, 0, 0, 0, 1], 0, 1),
+    ("tiled_d384", "tiled", 600, 384, 256, [200, 57, 0, 0, 300, 0, 1, 9], 0, 1),
+    # down projection split into partial sums over h
+    ("tiled_partials", "tiled", 600, 384, 512, [200, 57, 0, 0, 300, 0, 1, 9], 1, 4),
+    ("tiled_partials_h1024", "tiled", 300, 256, 1024, [0, 256, 1, 0, 300, 0, 0, 40], 1, 4),
+    # >= 256 rows per expert on average: 384-token tiles in the down projection,
+    # >= 1024: in the gate-up projection too (segments of 1, 384, 385 and > 1024 rows)
+    ("tiled_down384", "tiled", 1200, 384, 256, [500, 0, 385, 383, 1, 0, 700, 400], 0, 1),
+    ("tiled384", "tiled", 4096, 256, 384, [0, 1500, 1, 384, 769, 0, 2000, 3000], 0, 1),
+    ("tiled384_partials2", "tiled", 4096, 256, 512, [0, 1500, 1, 384, 769, 0, 2000, 3000], 1, 2),
+    ("tiled384_partials4", "tiled", 4096, 256, 1024, [3000, 1, 0, 385, 0, 1500, 2000, 769], 1, 4),
 ]
 
 
-@pytest.mark.parametrize("name,path,T,d,h,counts,flags", EXPERT_CASES,
+@pytest.mark.parametrize("name,path,T,d,h,counts,flags,parts_expected", EXPERT_CASES,
                          ids=[c[0] for c in EXPERT_CASES])
-def test_expert_steps(moe, oracle, name, path, T, d, h, counts, flags):
+def test_expert_steps(moe, oracle, name, path, T, d, h, counts, flags, parts_expected):
     E, K = len(counts), 2
     S = T * K
     off = _segments(counts)
     assert off[-1] <= S
+    _say(f"expert steps {name}: T={T} d={d} h={h} counts={counts}")
     cfg = mi.Config("ex", T=S, d=d, h=h, E=E, K=K, x_kind="rmsnorm")
     inp = mi.make_inputs(cfg, seed=7)
     xp = inp["x"]  # [S, d] rows already "permuted"
     act_in = mi.make_act(S, h, "bf16", seed=8)
     p = moe.problem(T, d, h, E, K, "bf16", "f32", path, flags)
     parts = moe.down_parts(p)
-    assert parts == (2 if flags else 1)
+    assert parts == parts_expected
     dev_x = parity.device_array(xp, "bf16")
     dev_off = parity.device_array(off, "i32")
     w1 = parity.device_array(inp["w1"], "bf16")
@@ -423,7 +430,7 @@ def test_combine_adds_partials(moe):
     T, K, d, h = 300, 2, 256, 512
     p = moe.problem(T, d, h, 8, K, "bf16", "f32", "tiled", moe.FLAG_DOWN_PARTIALS)
     parts = moe.down_parts(p)
-    assert parts == 2
+    assert parts == 4
     S = T * K
     rng = np.random.default_rng(10)
     o = rng.standard_normal((parts, S, d)).astype(np.float32)
@@ -433,7 +440,10 @@ def test_combine_adds_partials(moe):
                     parity.device_array(w, "f32"))
     torch.cuda.synchronize()
     y = parity.host_array(y).astype(np.float64)
-    row = (o[0] + o[1]).astype(np.float64)  # float32 sum of the parts, then weighted
+    row = o[0].copy()
+    for q in range(1, parts):  # float32 sum of the parts in order, then weighted
+        row += o[q]
+    row = row.astype(np.float64)
     ref = sum(w[:, k:k + 1].astype(np.float64) * row[slot[:, k]] for k in range(K))
     assert np.max(np.abs(y - ref)) <= 1e-6 * np.max(np.abs(ref))
 
@@ -446,7 +456,8 @@ def test_staged_with_partials_equals_forward(moe, oracle):
     y_fwd = _run_forward(moe, cfg, inp, "tiled")[0]
     p = moe.problem(cfg.T, cfg.d, cfg.h, cfg.E, cfg.K, "bf16", "f32", "tiled",
                     moe.FLAG_DOWN_PARTIALS)
-    assert moe.down_parts(p) == 2
+    parts = moe.down_parts(p)
+    assert parts == 4
     dev = parity.upload_inputs(inp, "bf16")
     idx, w, _ = moe.route(p, dev["x"], dev["w_g"])
     offsets, perm, slot, x_perm = moe.permute(p, dev["x"], idx)
@@ -454,7 +465,7 @@ def test_staged_with_partials_equals_forward(moe, oracle):
     o = moe.expert_down(p, act, offsets, dev["w2"])
     y = moe.combine(p, o, slot, w)
     torch.cuda.synchronize()
-    assert tuple(o.shape) == (2, cfg.T * cfg.K, cfg.d)
+    assert tuple(o.shape) == (parts, cfg.T * cfg.K, cfg.d)
     assert np.array_equal(parity.host_array(y).astype(np.float64), y_fwd)
     toks, y_ref, _, _ = _layer_ref(oracle, inp, cfg, np.arange(cfg.T), parity.host_array(idx),
                                    parity.host_array(w))
