@@ -103,21 +103,32 @@ moe_status hip_result(hipError_t e, const char *what) {
   return MOE_OK;
 }
 
-// Token tile of the tiled bf16 kernels: 384 tokens once an expert holds that
-// many rows on average (fewer bytes from L2 per flop), else 256 (less padding).
-// Measured on MI355X at d = 4096, h = 14336: the gate-up projection gains from
-// 384 at >= 1024 rows per expert, the down projection from >= 256.
+// Token tile of the tiled bf16 kernels, from the rows an expert holds on
+// average: 64 or 128 tokens while the weights are read once and most matrix
+// work would be padding, 256 in between, 384 once experts hold many rows (fewer
+// bytes from L2 per flop). The thresholds are where each measured fastest on
+// MI355X at d = 4096, h = 14336.
 constexpr int64_t kCUs = 256;
 
 int64_t rows_per_expert(const moe_problem *p) { return (p->T * p->K + p->E - 1) / p->E; }
 
-int gate_up_tile(const moe_problem *p) { return rows_per_expert(p) >= 1024 ? 384 : 256; }
-int down_tile(const moe_problem *p) { return rows_per_expert(p) >= 256 ? 384 : 256; }
+int gate_up_tile(const moe_problem *p) {
+  const int64_t n = rows_per_expert(p);
+  return n <= 64 ? 64 : n <= 96 ? 128 : n < 1024 ? 256 : 384;
+}
+int down_tile(const moe_problem *p) {
+  const int64_t n = rows_per_expert(p);
+  return n <= 48 ? 64 : n <= 96 ? 128 : n < 256 ? 256 : 384;
+}
+// workgroups of the down projection that run at once: two per compute unit
+// for 64-token tiles (80 KiB of LDS each), one otherwise
+int64_t down_slots(int bt) { return bt == 64 ? 2 * kCUs : kCUs; }
 
 // Partial sums of the down projection (see MOE_FLAG_DOWN_PARTIALS): the tiled
 // kernel can cut the sum over h into 2 or 4 parts, each a workgroup of its own,
 // so that the last, partly filled round of workgroups (one per compute unit at
-// a time) costs less. Estimated cost of p parts, in k-blocks of one round:
+// a time, two for 64-token tiles) costs less. Estimated cost of p parts, in
+// k-blocks of one round:
 // rounds(p) * (k-blocks per part + 8 for a tile's set-up and epilogue), plus
 // the extra float32 partial sums written and read again (about 13.5 MB per
 // unit at the measured ~5 TB/s). Tiles are estimated from an even split of the
@@ -134,7 +145,7 @@ int down_parts(const moe_problem *p) {
   double best_cost = 0.0;
   for (int parts = 1; parts <= 4; parts *= 2) {
     if (nk % (2 * parts)) break;  // each part needs an even count of 64-wide k-blocks
-    const int64_t rounds = (tiles * parts + kCUs - 1) / kCUs;
+    const int64_t rounds = (tiles * parts + down_slots(int(bt)) - 1) / down_slots(int(bt));
     const double cost = double(rounds) * double(nk / parts + 8) +
                         double(parts - 1) * double(S) * double(p->d) * 8.0 / unit_bytes;
     if (parts == 1 || cost < best_cost) {

@@ -297,6 +297,194 @@ __global__ __launch_bounds__(512) void tiled_kernel(const uint16_t *__restrict__
   }
 }
 
+// One global -> LDS copy of 16 bytes per lane (a plain function: the builtin
+// inside a kernel template can fail the template's host-side instantiation).
+__device__ __forceinline__ void dma16(const uint16_t *g, lds_void *l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+// Small batches (an expert holds a few dozen rows): the weight tiles are read
+// from HBM once and the matrix work is mostly padding, so the tile narrows to
+// BT = 64 or 128 tokens (256 weight rows as before). 8 wavefronts in a 4 x 2
+// grid, each 64 weight rows x BT/2 tokens (2 x BT/64 accumulators); for gate-up
+// a wavefront's 64 rows are 32 W1 and the same 32 W3 rows. BT = 64 needs 80 KiB
+// of LDS, so two workgroups share a compute unit and keep more bytes in flight.
+template <bool GATEUP, int BT>
+__global__ __launch_bounds__(512) void tiled_small_kernel(
+    const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
+    const uint16_t *__restrict__ Wa, const uint16_t *__restrict__ Wb, void *__restrict__ out,
+    int N, int K, int ksplit, int64_t part_stride) {
+  constexpr int NT = BT / 64;  // 32-token accumulator columns per wavefront
+  constexpr int XI = BT / 64;  // token-row DMA instructions per wavefront
+  constexpr int kCols = GATEUP ? 128 : 256;
+  const int ct = (N + kCols - 1) / kCols;
+  int total = 0;
+  for (int q = 0; q < E; ++q) total += ct * ((offsets[q + 1] - offsets[q] + BT - 1) / BT);
+  const int g8 = (total * ksplit + kXCD - 1) / kXCD;
+  const int b = blockIdx.x;
+  if (b >= g8 * kXCD) return;
+  int L = (b % kXCD) * g8 + b / kXCD;
+  if (L >= total * ksplit) return;
+  const int ks = L / total;
+  L -= ks * total;
+  int e = 0, row0 = 0, ne = 0, mtiles = 0;
+  for (; e < E; ++e) {
+    row0 = offsets[e];
+    ne = offsets[e + 1] - row0;
+    mtiles = (ne + BT - 1) / BT;
+    if (L < ct * mtiles) break;
+    L -= ct * mtiles;
+  }
+  const int cb = L / mtiles;
+  const int m0 = (L % mtiles) * BT;
+  const int c0 = cb * kCols;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t sW0[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX0[BT * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX1[BT * 64];
+
+  // ---- DMA assignment as in tiled_kernel: wave w fills weight rows
+  // [32w, 32w+32) (for gate-up: W1 rows if w is even, else the W3 rows of the
+  // same 32 columns) and token rows [w*BT/8, (w+1)*BT/8).
+  const size_t mat_elems = size_t(N) * K;
+  const uint16_t *wmat = Wa + size_t(e) * mat_elems;
+  if (GATEUP && (wave & 1)) wmat = Wb + size_t(e) * mat_elems;
+  const uint16_t *x_t = X + size_t(row0 + m0) * K;
+  const int xlim = ne - 1 - m0;
+  const int dma_row = wave * 32;
+  const int dma_xrow = wave * (BT / 8);
+  uint32_t wofs[4], xofs[XI];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = lane >> 3;
+    const int c = (lane & 7) ^ lr ^ i;  // swz of row 8i + lr in its 32-row group
+    int wrow;
+    if constexpr (GATEUP) wrow = c0 + (wave >> 1) * 32 + 8 * i + lr;
+    else wrow = min(c0 + dma_row + 8 * i + lr, N - 1);
+    wofs[i] = uint32_t(wrow) * uint32_t(K) + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int lr = lane >> 3;
+    const int q = (dma_xrow / 8 + i) & 3;
+    xofs[i] = uint32_t(min(dma_xrow + 8 * i + lr, xlim)) * uint32_t(K) +
+              (((lane & 7) ^ lr ^ q) << 3);
+  }
+
+  // ---- fragment read addresses (bytes): row (lane & 31) of a 32-row group,
+  // logical chunk kk*2 + (lane >> 5)
+  const int g = (lane >> 5) ^ swz(lane & 31);
+  uint32_t offk[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) offk[kk] = uint32_t(((kk * 2) ^ g) * 16);
+  const uint32_t baseA = uint32_t((wr * 64 + (lane & 31)) * 128);
+  const uint32_t baseB = uint32_t((wc * (BT / 2) + (lane & 31)) * 128);
+
+  f32x16 acc[2][NT];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[f][t][i] = 0.f;
+
+  const int nk = K / 64 / ksplit;  // k-blocks of this part (an even count)
+  const int kb0 = ks * nk;
+
+#define DMA(SW, SX, KB)                                                                    \
+  {                                                                                        \
+    const uint32_t k0 = uint32_t((kb0 + min(KB, nk - 1)) * 64);                            \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
+      dma16(wmat + wofs[i] + k0, (lds_void *)(SW + (dma_row + i * 8) * 64));              \
+    _Pragma("unroll") for (int i = 0; i < XI; ++i)                                         \
+      dma16(x_t + xofs[i] + k0, (lds_void *)(SX + (dma_xrow + i * 8) * 64));              \
+  }
+#define COMPUTE(SW, SX)                                                                    \
+  {                                                                                        \
+    const char *pa = reinterpret_cast<const char *>(SW) + baseA;                           \
+    const char *pb = reinterpret_cast<const char *>(SX) + baseB;                           \
+    bf16x8 fa[2][2], fb[2][NT];                                                            \
+    _Pragma("unroll") for (int f = 0; f < 2; ++f)                                          \
+      fa[0][f] = *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[0]);               \
+    _Pragma("unroll") for (int t = 0; t < NT; ++t)                                         \
+      fb[0][t] = *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[0]);               \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                     \
+      const int cur = kk & 1;                                                              \
+      if (kk + 1 < 4) {                                                                    \
+        _Pragma("unroll") for (int f = 0; f < 2; ++f) fa[cur ^ 1][f] =                     \
+            *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[kk + 1]);               \
+        _Pragma("unroll") for (int t = 0; t < NT; ++t) fb[cur ^ 1][t] =                    \
+            *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[kk + 1]);               \
+      }                                                                                    \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 + NT, 1);                              \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NT, 1);                              \
+      _Pragma("unroll") for (int t = 0; t < NT; ++t)                                       \
+        _Pragma("unroll") for (int f = 0; f < 2; ++f)                                      \
+          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][f], fb[cur][t],      \
+                                                              acc[f][t], 0, 0, 0);         \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+    }                                                                                      \
+  }
+
+  DMA(sW0, sX0, 0)
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    DMA(sW1, sX1, kt + 1)
+    COMPUTE(sW0, sX0)
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    DMA(sW0, sX0, kt + 2)
+    COMPUTE(sW1, sX1)
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
+#undef DMA
+#undef COMPUTE
+
+  // ---- epilogue (fragment layout as in tiled_kernel)
+  const int ih = 4 * (lane >> 5);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tok = m0 + wc * (BT / 2) + t * 32 + (lane & 31);
+    if (tok >= ne) continue;
+    const size_t orow = size_t(row0 + tok) * N + size_t(ks) * size_t(part_stride);
+    if constexpr (GATEUP) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = c0 + wr * 32 + 8 * q + ih;
+        if (col >= N) continue;
+        float v[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) v[s] = silu(acc[0][t][4 * q + s]) * acc[1][t][4 * q + s];
+        uint2 pk;
+        pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+        pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + orow + col) = pk;
+      }
+    } else {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = c0 + wr * 64 + f * 32 + 8 * q + ih;
+          if (col >= N) continue;
+          *reinterpret_cast<float4 *>(static_cast<float *>(out) + orow + col) =
+              make_float4(acc[f][t][4 * q], acc[f][t][4 * q + 1], acc[f][t][4 * q + 2],
+                          acc[f][t][4 * q + 3]);
+        }
+      }
+    }
+  }
+}
+
 // Upper bound of the tile count for any split of S rows over E experts.
 inline unsigned tiled_grid(int64_t S, int E, int N, int cols, int bt, int ksplit) {
   const int64_t ct = (N + cols - 1) / cols;
@@ -314,6 +502,17 @@ void launch_t(const void *x, const int32_t *offsets, const void *wa, const void 
                      K, ksplit, part_stride);
 }
 
+template <bool GATEUP, int BT>
+void launch_small(const void *x, const int32_t *offsets, const void *wa, const void *wb,
+                  void *out, int E, int64_t S, int N, int K, int ksplit, int64_t part_stride,
+                  hipStream_t s) {
+  hipLaunchKernelGGL((tiled_small_kernel<GATEUP, BT>),
+                     dim3(tiled_grid(S, E, N, GATEUP ? 128 : 256, BT, ksplit)), dim3(512), 0, s,
+                     static_cast<const uint16_t *>(x), offsets, E,
+                     static_cast<const uint16_t *>(wa), static_cast<const uint16_t *>(wb), out, N,
+                     K, ksplit, part_stride);
+}
+
 }  // namespace
 
 hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
@@ -321,6 +520,10 @@ hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, cons
                                 int bt, hipStream_t s) {
   if (bt == 384)
     launch_t<true, 384>(x_perm, offsets, w1, w3, act, E, S, h, d, 1, 0, s);
+  else if (bt == 128)
+    launch_small<true, 128>(x_perm, offsets, w1, w3, act, E, S, h, d, 1, 0, s);
+  else if (bt == 64)
+    launch_small<true, 64>(x_perm, offsets, w1, w3, act, E, S, h, d, 1, 0, s);
   else
     launch_t<true, 256>(x_perm, offsets, w1, w3, act, E, S, h, d, 1, 0, s);
   return hipGetLastError();
@@ -331,6 +534,10 @@ hipError_t launch_tiled_down(const void *act, const int32_t *offsets, const void
                              hipStream_t s) {
   if (bt == 384)
     launch_t<false, 384>(act, offsets, w2, nullptr, o_perm, E, S, d, h, parts, S * d, s);
+  else if (bt == 128)
+    launch_small<false, 128>(act, offsets, w2, nullptr, o_perm, E, S, d, h, parts, S * d, s);
+  else if (bt == 64)
+    launch_small<false, 64>(act, offsets, w2, nullptr, o_perm, E, S, d, h, parts, S * d, s);
   else
     launch_t<false, 256>(act, offsets, w2, nullptr, o_perm, E, S, d, h, parts, S * d, s);
   return hipGetLastError();

@@ -73,8 +73,8 @@ def test_bad_dtype_and_flags():
 
 def test_path_resolution():
     # the automatic switch point comes from a batch-size sweep on MI355X (bench.py --sweep)
-    assert moe.resolve_path(_p(T=192)) == binding.PATH_STREAM
-    assert moe.resolve_path(_p(T=193)) == binding.PATH_TILED
+    assert moe.resolve_path(_p(T=112)) == binding.PATH_STREAM
+    assert moe.resolve_path(_p(T=113)) == binding.PATH_TILED
     assert moe.resolve_path(_p(T=4096, path="stream")) == binding.PATH_STREAM
     assert moe.resolve_path(_p(T=8, path="tiled")) == binding.PATH_TILED
     assert moe.resolve_path(_p(dtype="f32")) == binding.PATH_TILED
@@ -104,7 +104,8 @@ def test_down_parts():
     assert moe.down_parts(_p(T=1024, d=1024, h=14336, flags=P)) == 4   # 32 tiles
     assert moe.down_parts(_p(T=4096, d=4096, h=14336 + 128, flags=P)) == 1  # 226 k-blocks
     assert moe.down_parts(_p(T=32, d=4096, h=14336, flags=P)) == 1      # streaming path
-    assert moe.down_parts(_p(T=32, d=4096, h=14336, flags=P, path="tiled")) == 2
+    # 64-token tiles: two workgroups per compute unit, 128 tiles fit one round 4 times
+    assert moe.down_parts(_p(T=32, d=4096, h=14336, flags=P, path="tiled")) == 4
     assert moe.down_parts(_p(T=64, d=128, h=256, dtype="f32", flags=P)) == 1
     # the layer's own workspace makes room for the partial sums it uses
     S, d, h = 4096 * 2, 4096, 14336

@@ -60,8 +60,9 @@ SMALL = [
     ("tiny_f32", mi.CONFIGS["tiny_f32"], "auto"),
     ("bf16_tiled_ragged", mi.Config("s1", T=1000, d=256, h=640, wg_std="fan_in_d"), "tiled"),
     ("bf16_tiled_T65", mi.Config("s2", T=65, d=384, h=256, wg_std="fan_in_d"), "tiled"),
-    ("bf16_auto_T193_tiled", mi.Config("s2b", T=193, d=384, h=256, wg_std="fan_in_d"), "auto"),
-    ("bf16_auto_T192_stream", mi.Config("s2c", T=192, d=256, h=384, wg_std="fan_in_d"), "auto"),
+    ("bf16_auto_T113_tiled", mi.Config("s2b", T=113, d=384, h=256, wg_std="fan_in_d"), "auto"),
+    ("bf16_auto_T112_stream", mi.Config("s2c", T=112, d=256, h=384, wg_std="fan_in_d"), "auto"),
+    ("bf16_tiled_T193", mi.Config("s2d", T=193, d=384, h=256, wg_std="fan_in_d"), "tiled"),
     ("bf16_stream_T64", mi.Config("s3", T=64, d=512, h=1024, wg_std="fan_in_d"), "auto"),
     ("bf16_stream_T7", mi.Config("s4", T=7, d=256, h=384, wg_std="fan_in_d"), "stream"),
     ("bf16_stream_T100_multigroup", mi.Config("s5", T=100, d=256, h=256, wg_std="fan_in_d"),
@@ -350,6 +351,9 @@ EXPERT_CASES = [
     # down projection split into partial sums over h
     ("tiled_partials", "tiled", 600, 384, 512, [200, 57, 0, 0, 300, 0, 1, 9], 1, 4),
     ("tiled_partials_h1024", "tiled", 300, 256, 1024, [0, 256, 1, 0, 300, 0, 0, 40], 1, 4),
+    # a few dozen rows per expert on average: 64- and 128-token tiles
+    ("tiled64", "tiled", 100, 256, 512, [0, 70, 1, 64, 65, 0, 0, 0], 1, 4),
+    ("tiled128", "tiled", 350, 256, 512, [129, 0, 128, 127, 1, 0, 200, 115], 1, 4),
     # >= 256 rows per expert on average: 384-token tiles in the down projection,
     # >= 1024: in the gate-up projection too (segments of 1, 384, 385 and > 1024 rows)
     ("tiled_down384", "tiled", 1200, 384, 256, [500, 0, 385, 383, 1, 0, 700, 400], 0, 1),
