@@ -208,18 +208,22 @@ moe_status do_route(const moe_problem *p, const void *x, const void *w_g, int32_
                     "route launch");
 }
 
+// x_perm == nullptr: the index arrays only (the caller reads x through perm).
 moe_status do_permute(const moe_problem *p, const void *x, const int32_t *idx, int32_t *offsets,
                       int32_t *perm, int32_t *slot, void *x_perm, hipStream_t s) {
   const int64_t S = p->T * p->K;
   CHECK(hip_result(moe::launch_permute_index(idx, S, p->K, p->E, p->capacity, offsets, perm, slot, s),
                    "permute launch"));
+  if (!x_perm) return MOE_OK;
   return hip_result(moe::launch_gather_rows(x, perm, offsets, p->E, S, p->d * esize(p->dtype),
                                             x_perm, s),
                     "gather launch");
 }
 
+// rowmap (nullable, STREAM path only): sorted row r is row rowmap[r] of x_perm.
 moe_status do_gate_up(const moe_problem *p, const void *x_perm, const int32_t *offsets,
-                      const void *w1, const void *w3, void *act, hipStream_t s) {
+                      const void *w1, const void *w3, void *act, hipStream_t s,
+                      const int32_t *rowmap = nullptr) {
   const int64_t S = p->T * p->K;
   hipError_t e;
   if (p->dtype == MOE_F32)
@@ -227,8 +231,8 @@ moe_status do_gate_up(const moe_problem *p, const void *x_perm, const int32_t *o
                                 static_cast<const float *>(w1), static_cast<const float *>(w3),
                                 static_cast<float *>(act), p->E, S, int(p->d), int(p->h), s);
   else if (resolve(p) == MOE_PATH_STREAM)
-    e = moe::launch_stream_gate_up(x_perm, offsets, w1, w3, act, p->E, int(p->d), int(p->h), p->T,
-                                   S, s);
+    e = moe::launch_stream_gate_up(x_perm, rowmap, offsets, w1, w3, act, p->E, int(p->d),
+                                   int(p->h), p->T, S, s);
   else
     e = moe::launch_tiled_gate_up(x_perm, offsets, w1, w3, act, p->E, S, int(p->d), int(p->h),
                                   gate_up_tile(p), s);
@@ -304,8 +308,15 @@ moe_status run_layer(const moe_problem *p, const void *x, const void *w_g, const
   float *o_perm = reinterpret_cast<float *>(base + L.o_perm);
   const hipStream_t s = as_stream(stream);
   CHECK(do_route(p, x, w_g, idx, w, nullptr, s));
-  CHECK(do_permute(p, x, idx, offsets, perm, slot, x_perm, s));
-  CHECK(do_gate_up(p, x_perm, offsets, w1, w3, act, s));
+  if (p->dtype == MOE_BF16 && resolve(p) == MOE_PATH_STREAM) {
+    // the streaming gate-up reads each token row of x through perm_token, so
+    // the layer needs no gathered copy of x
+    CHECK(do_permute(p, x, idx, offsets, perm, slot, nullptr, s));
+    CHECK(do_gate_up(p, x, offsets, w1, w3, act, s, perm));
+  } else {
+    CHECK(do_permute(p, x, idx, offsets, perm, slot, x_perm, s));
+    CHECK(do_gate_up(p, x_perm, offsets, w1, w3, act, s));
+  }
   CHECK(do_down(p, act, offsets, w2, o_perm, L.parts, s));
   CHECK(do_combine(p, o_perm, L.parts, slot, w, residual, y, s));
   return ok();

@@ -61,8 +61,11 @@ __device__ __forceinline__ bf16x8 ld16(const uint16_t *p) {
 }
 
 // One group of at most 16*MT rows of expert e (rows row0 .. row0 + ne - 1).
+// With a row map, sorted row r is row rowmap[r] of X (the layer reads the token
+// rows straight from its input instead of a gathered copy).
 template <int NMAT, int NT, int MT, int PD>
 __device__ __forceinline__ void stream_rows(const uint16_t *__restrict__ X,
+                                            const int32_t *__restrict__ rowmap,
                                             const uint16_t *__restrict__ Wa,
                                             const uint16_t *__restrict__ Wb,
                                             void *__restrict__ out, int N, int K, int e, int cb,
@@ -95,8 +98,10 @@ __device__ __forceinline__ void stream_rows(const uint16_t *__restrict__ X,
   // B operand: lane (r16, g) holds token row r16, k-piece g of a 32-wide k half
   const uint16_t *xsrc[MT];
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-    xsrc[mi] = X + size_t(row0 + min(mi * 16 + r16, ne - 1)) * K + g * 8;
+  for (int mi = 0; mi < MT; ++mi) {
+    const int r = row0 + min(mi * 16 + r16, ne - 1);
+    xsrc[mi] = X + size_t(rowmap ? rowmap[r] : r) * K + g * 8;
+  }
   // A operand: lane (r16, g) reads weight row r16 of a tile, logical piece 4 hh + g
   uint32_t offA[2];
 #pragma unroll
@@ -229,6 +234,7 @@ __device__ __forceinline__ void stream_rows(const uint16_t *__restrict__ X,
 // weights; workgroups of a row group an expert does not have exit at once.
 template <int NMAT, int NT, int KMT, int PD>
 __global__ __launch_bounds__(64 * kSplitK) void stream_kernel(const uint16_t *__restrict__ X,
+                                                              const int32_t *__restrict__ rowmap,
                                                               const int32_t *__restrict__ offsets,
                                                               const uint16_t *__restrict__ Wa,
                                                               const uint16_t *__restrict__ Wb,
@@ -248,13 +254,13 @@ __global__ __launch_bounds__(64 * kSplitK) void stream_kernel(const uint16_t *__
   const int mt = (rows + 15) >> 4;
   lds_char *l = (lds_char *)lds;
   if (mt == 1)
-    stream_rows<NMAT, NT, 1, PD>(X, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
+    stream_rows<NMAT, NT, 1, PD>(X, rowmap, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
   else if (KMT >= 2 && mt == 2)
-    stream_rows<NMAT, NT, (KMT >= 2 ? 2 : 1), PD>(X, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
+    stream_rows<NMAT, NT, (KMT >= 2 ? 2 : 1), PD>(X, rowmap, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
   else if (KMT >= 3 && mt == 3)
-    stream_rows<NMAT, NT, (KMT >= 3 ? 3 : 1), PD>(X, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
+    stream_rows<NMAT, NT, (KMT >= 3 ? 3 : 1), PD>(X, rowmap, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
   else
-    stream_rows<NMAT, NT, KMT, PD>(X, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
+    stream_rows<NMAT, NT, KMT, PD>(X, rowmap, Wa, Wb, out, N, K, e, cb, seg0 + rg, rows, l);
 }
 
 // Measured on MI355X (decode, 8 experts of 14336 x 4096): gate-up with 2 x 32
@@ -268,9 +274,11 @@ constexpr int kNTDownSmall = 2, kNTDownLarge = 4, kPDDown = 2;
 // rows_hint: the rows an expert usually has at most (T for a routed batch, whose
 // experts get one row per token at most); it selects how many token tiles the
 // accumulators hold. rows_bound: a bound no segment can exceed (S = offsets[E]
-// at most); it sets how many row groups the grid provides.
-hipError_t launch_stream_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
-                                 const void *w3, void *act, int E, int d, int h, int64_t rows_hint,
+// at most); it sets how many row groups the grid provides. rowmap (nullable):
+// sorted row r of the gate-up input is row rowmap[r] of x_perm.
+hipError_t launch_stream_gate_up(const void *x_perm, const int32_t *rowmap,
+                                 const int32_t *offsets, const void *w1, const void *w3,
+                                 void *act, int E, int d, int h, int64_t rows_hint,
                                  int64_t rows_bound, hipStream_t s) {
   auto X = static_cast<const uint16_t *>(x_perm);
   auto A = static_cast<const uint16_t *>(w1);
@@ -280,12 +288,12 @@ hipError_t launch_stream_gate_up(const void *x_perm, const int32_t *offsets, con
     const int nz = int((rows_bound + 31) / 32);
     hipLaunchKernelGGL((stream_kernel<2, kNTGateUp, 2, kPDGateUp>),
                        dim3(unsigned(ncb), unsigned(E), unsigned(nz)), dim3(64 * kSplitK), 0, s, X,
-                       offsets, A, B, act, h, d);
+                       rowmap, offsets, A, B, act, h, d);
   } else {
     const int nz = int((rows_bound + 63) / 64);
     hipLaunchKernelGGL((stream_kernel<2, kNTGateUp, 4, kPDGateUp>),
                        dim3(unsigned(ncb), unsigned(E), unsigned(nz)), dim3(64 * kSplitK), 0, s, X,
-                       offsets, A, B, act, h, d);
+                       rowmap, offsets, A, B, act, h, d);
   }
   return hipGetLastError();
 }
@@ -302,13 +310,13 @@ hipError_t launch_stream_down(const void *act, const int32_t *offsets, const voi
     const int ncb = d / (16 * kNTDownSmall);
     hipLaunchKernelGGL((stream_kernel<1, kNTDownSmall, 2, kPDDown>),
                        dim3(unsigned(ncb), unsigned(E), unsigned(nz)), dim3(64 * kSplitK), 0, s, X,
-                       offsets, A, B, O, d, h);
+                       static_cast<const int32_t *>(nullptr), offsets, A, B, O, d, h);
   } else {
     const int nz = int((rows_bound + 63) / 64);
     const int ncb = d / (16 * kNTDownLarge);
     hipLaunchKernelGGL((stream_kernel<1, kNTDownLarge, 4, kPDDown>),
                        dim3(unsigned(ncb), unsigned(E), unsigned(nz)), dim3(64 * kSplitK), 0, s, X,
-                       offsets, A, B, O, d, h);
+                       static_cast<const int32_t *>(nullptr), offsets, A, B, O, d, h);
   }
   return hipGetLastError();
 }

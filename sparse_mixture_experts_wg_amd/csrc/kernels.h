@@ -46,8 +46,11 @@ hipError_t launch_gather_rows(const void *x, const int32_t *perm_token, const in
 // or 64, each group streaming its weights). rows_hint: usual largest segment
 // (T); rows_bound: no segment is longer (S); the grid's z extent is
 // rows_bound / 32 or / 64, which the caller keeps below 2^16.
-hipError_t launch_stream_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
-                                 const void *w3, void *act, int E, int d, int h, int64_t rows_hint,
+// rowmap (nullable): sorted row r of the gate-up input is row rowmap[r] of x_perm
+// (the layer passes the unsorted input x and perm_token, skipping the gather).
+hipError_t launch_stream_gate_up(const void *x_perm, const int32_t *rowmap,
+                                 const int32_t *offsets, const void *w1, const void *w3,
+                                 void *act, int E, int d, int h, int64_t rows_hint,
                                  int64_t rows_bound, hipStream_t s);
 hipError_t launch_stream_down(const void *act, const int32_t *offsets, const void *w2,
                               float *o_perm, int E, int d, int h, int64_t rows_hint,

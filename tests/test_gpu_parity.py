@@ -452,6 +452,25 @@ def test_combine_adds_partials(moe):
     assert np.max(np.abs(y - ref)) <= 1e-6 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("T,cap", [(40, 0), (100, 0), (60, 9)])
+def test_stream_forward_equals_staged(moe, T, cap):
+    """On the streaming path moe_forward reads the token rows of x through perm_token
+    instead of a gathered copy; the staged entry points gather with moe_permute.
+    Same kernels otherwise: bit-identical outputs (also under a capacity cap)."""
+    cfg = mi.Config("sf", T=T, d=256, h=384, wg_std="fan_in_d")
+    inp = mi.make_inputs(cfg, seed=12)
+    p = moe.problem(T, cfg.d, cfg.h, cfg.E, cfg.K, "bf16", "f32", "stream", 0, cap)
+    dev = parity.upload_inputs(inp, "bf16")
+    y_fwd = moe.forward(p, dev["x"], dev["w_g"], dev["w1"], dev["w3"], dev["w2"])
+    idx, w, _ = moe.route(p, dev["x"], dev["w_g"])
+    offsets, perm, slot, x_perm = moe.permute(p, dev["x"], idx)
+    act = moe.expert_gate_up(p, x_perm, offsets, dev["w1"], dev["w3"])
+    o = moe.expert_down(p, act, offsets, dev["w2"])
+    y = moe.combine(p, o, slot, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(parity.host_array(y), parity.host_array(y_fwd))
+
+
 def test_staged_with_partials_equals_forward(moe, oracle):
     """The staged entry points with MOE_FLAG_DOWN_PARTIALS run the same kernels as
     moe_forward (which always allows partial sums): bit-identical outputs."""
