@@ -59,6 +59,8 @@ SMALL = [
     # name, config, path
     ("tiny_f32", mi.CONFIGS["tiny_f32"], "auto"),
     ("bf16_tiled_ragged", mi.Config("s1", T=1000, d=256, h=640, wg_std="fan_in_d"), "tiled"),
+    # >= 1024 rows per expert: 384-token tiles in both projections, down in 2 parts
+    ("bf16_tiled384_T4096", mi.Config("s1b", T=4096, d=256, h=512, wg_std="fan_in_d"), "auto"),
     ("bf16_tiled_T65", mi.Config("s2", T=65, d=384, h=256, wg_std="fan_in_d"), "tiled"),
     ("bf16_auto_T113_tiled", mi.Config("s2b", T=113, d=384, h=256, wg_std="fan_in_d"), "auto"),
     ("bf16_auto_T112_stream", mi.Config("s2c", T=112, d=256, h=384, wg_std="fan_in_d"), "auto"),
