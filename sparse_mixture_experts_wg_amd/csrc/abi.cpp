@@ -105,55 +105,43 @@ moe_status hip_result(hipError_t e, const char *what) {
 
 // Token tile of the tiled bf16 kernels, from the rows an expert holds on
 // average: 64 or 128 tokens while the weights are read once and most matrix
-// work would be padding, 256 in between, 384 once experts hold many rows (fewer
-// bytes from L2 per flop). The thresholds are where each measured fastest on
-// MI355X at d = 4096, h = 14336.
+// work would be padding, 256 above. The thresholds are where each measured
+// fastest on MI355X at d = 4096, h = 14336.
 constexpr int64_t kCUs = 256;
 
 int64_t rows_per_expert(const moe_problem *p) { return (p->T * p->K + p->E - 1) / p->E; }
 
 int gate_up_tile(const moe_problem *p) {
   const int64_t n = rows_per_expert(p);
-  return n <= 64 ? 64 : n <= 96 ? 128 : n < 1024 ? 256 : 384;
+  return n <= 64 ? 64 : n <= 96 ? 128 : 256;
 }
 int down_tile(const moe_problem *p) {
   const int64_t n = rows_per_expert(p);
-  return n <= 48 ? 64 : n <= 96 ? 128 : n < 256 ? 256 : 384;
+  return n <= 48 ? 64 : n <= 96 ? 128 : 256;
 }
-// workgroups of the down projection that run at once: two per compute unit
-// for 64-token tiles (80 KiB of LDS each), one otherwise
-int64_t down_slots(int bt) { return bt == 64 ? 2 * kCUs : kCUs; }
 
 // Partial sums of the down projection (see MOE_FLAG_DOWN_PARTIALS): the tiled
 // kernel can cut the sum over h into 2 or 4 parts, each a workgroup of its own,
-// so that the last, partly filled round of workgroups (one per compute unit at
-// a time, two for 64-token tiles) costs less. Estimated cost of p parts, in
-// k-blocks of one round:
-// rounds(p) * (k-blocks per part + 8 for a tile's set-up and epilogue), plus
-// the extra float32 partial sums written and read again (about 13.5 MB per
-// unit at the measured ~5 TB/s). Tiles are estimated from an even split of the
-// rows over the experts.
+// so that few tiles still fill the GPU. Workgroups run one per compute unit at
+// a time (two for 64-token tiles). The tiles are estimated from an even split
+// of the rows plus one standard deviation of a random split (n + sqrt(n) rows
+// per expert): 4 parts when all of them fit one round, 1 part from 8 rounds
+// on, else 2 -- the choices that measured fastest on MI355X from T = 64 to
+// 16384 (d = 4096, h = 14336) and at d = 6144, h = 16384. Each part needs an
+// even count of 64-wide k-blocks.
 int down_parts(const moe_problem *p) {
   if (!(p->flags & MOE_FLAG_DOWN_PARTIALS) || p->dtype != MOE_BF16) return 1;
   if (resolve(p) != MOE_PATH_TILED) return 1;
   const int64_t bt = down_tile(p);
-  const int64_t S = p->T * p->K;
-  const int64_t tiles = ((p->d + 255) / 256) * p->E * ((rows_per_expert(p) + bt - 1) / bt);
+  const int64_t slots = bt == 64 ? 2 * kCUs : kCUs;
+  const int64_t n = rows_per_expert(p);
+  int64_t sd = 0;
+  while ((sd + 1) * (sd + 1) <= n) ++sd;  // floor(sqrt(n))
+  const int64_t tiles = ((p->d + 255) / 256) * p->E * ((n + sd + bt - 1) / bt);
   const int64_t nk = p->h / 64;
-  const double unit_bytes = 13.5e6 * double(bt) / 384.0;
-  int best = 1;
-  double best_cost = 0.0;
-  for (int parts = 1; parts <= 4; parts *= 2) {
-    if (nk % (2 * parts)) break;  // each part needs an even count of 64-wide k-blocks
-    const int64_t rounds = (tiles * parts + down_slots(int(bt)) - 1) / down_slots(int(bt));
-    const double cost = double(rounds) * double(nk / parts + 8) +
-                        double(parts - 1) * double(S) * double(p->d) * 8.0 / unit_bytes;
-    if (parts == 1 || cost < best_cost) {
-      best = parts;
-      best_cost = cost;
-    }
-  }
-  return best;
+  int parts = tiles * 4 <= slots ? 4 : (tiles + slots - 1) / slots >= 8 ? 1 : 2;
+  while (parts > 1 && nk % (2 * parts)) parts /= 2;
+  return parts;
 }
 
 struct ForwardLayout {

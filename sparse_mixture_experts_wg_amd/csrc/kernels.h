@@ -55,7 +55,7 @@ hipError_t launch_stream_gate_up(const void *x_perm, const int32_t *rowmap,
 hipError_t launch_stream_down(const void *act, const int32_t *offsets, const void *w2,
                               float *o_perm, int E, int d, int h, int64_t rows_hint,
                               int64_t rows_bound, hipStream_t s);
-// TILED path (bf16 matrix cores); bt: token tile, 64, 128, 256 or 384.
+// TILED path (bf16 matrix cores); bt: token tile, 64, 128 or 256.
 hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
                                 const void *w3, void *act, int E, int64_t S, int d, int h,
                                 int bt, hipStream_t s);

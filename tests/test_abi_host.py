@@ -92,19 +92,19 @@ def test_capacity_field():
 
 
 def test_down_parts():
-    """Partial sums only when asked for, on the tiled bf16 path, with an even count of
-    64-wide k-blocks per part; 1, 2 or 4 parts from the estimated cost of the last,
-    partly filled round of workgroups on 256 compute units."""
+    """Partial sums only when asked for, on the tiled bf16 path: 4 parts when they all fit
+    one round of workgroups, 1 from 8 rounds on, else 2; a part needs an even count of
+    64-wide k-blocks."""
     P = binding.FLAG_DOWN_PARTIALS
     assert moe.down_parts(_p(T=4096, d=4096, h=14336)) == 1
-    assert moe.down_parts(_p(T=4096, d=4096, h=14336, flags=P)) == 2   # 384 tiles: 3 rounds
-    assert moe.down_parts(_p(T=16384, d=4096, h=14336, flags=P)) == 1  # enough tiles
-    assert moe.down_parts(_p(T=2048, d=4096, h=14336, flags=P)) == 1   # 256 tiles: one round
-    assert moe.down_parts(_p(T=8192, d=6144, h=16384, flags=P)) == 2   # 4.5 rounds -> 9 / 2
+    assert moe.down_parts(_p(T=4096, d=4096, h=14336, flags=P)) == 2   # 640 tiles: 3 rounds
+    assert moe.down_parts(_p(T=16384, d=4096, h=14336, flags=P)) == 1  # 2176 tiles: 9 rounds
+    assert moe.down_parts(_p(T=2048, d=4096, h=14336, flags=P)) == 2
+    assert moe.down_parts(_p(T=8192, d=6144, h=16384, flags=P)) == 2   # 1728 tiles: 7 rounds
     assert moe.down_parts(_p(T=1024, d=1024, h=14336, flags=P)) == 4   # 32 tiles
     assert moe.down_parts(_p(T=4096, d=4096, h=14336 + 128, flags=P)) == 1  # 226 k-blocks
     assert moe.down_parts(_p(T=32, d=4096, h=14336, flags=P)) == 1      # streaming path
-    # 64-token tiles: two workgroups per compute unit, 128 tiles fit one round 4 times
+    # 64-token tiles: two workgroups per compute unit, 4 x 128 tiles fit one round
     assert moe.down_parts(_p(T=32, d=4096, h=14336, flags=P, path="tiled")) == 4
     assert moe.down_parts(_p(T=64, d=128, h=256, dtype="f32", flags=P)) == 1
     # the layer's own workspace makes room for the partial sums it uses

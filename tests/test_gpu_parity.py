@@ -59,8 +59,8 @@ SMALL = [
     # name, config, path
     ("tiny_f32", mi.CONFIGS["tiny_f32"], "auto"),
     ("bf16_tiled_ragged", mi.Config("s1", T=1000, d=256, h=640, wg_std="fan_in_d"), "tiled"),
-    # >= 1024 rows per expert: 384-token tiles in both projections, down in 2 parts
-    ("bf16_tiled384_T4096", mi.Config("s1b", T=4096, d=256, h=512, wg_std="fan_in_d"), "auto"),
+    # about 1024 rows per expert, every token compared
+    ("bf16_tiled_T4096", mi.Config("s1b", T=4096, d=256, h=512, wg_std="fan_in_d"), "auto"),
     ("bf16_tiled_T65", mi.Config("s2", T=65, d=384, h=256, wg_std="fan_in_d"), "tiled"),
     ("bf16_auto_T113_tiled", mi.Config("s2b", T=113, d=384, h=256, wg_std="fan_in_d"), "auto"),
     ("bf16_auto_T112_stream", mi.Config("s2c", T=112, d=256, h=384, wg_std="fan_in_d"), "auto"),
@@ -356,12 +356,12 @@ EXPERT_CASES = [
     # a few dozen rows per expert on average: 64- and 128-token tiles
     ("tiled64", "tiled", 100, 256, 512, [0, 70, 1, 64, 65, 0, 0, 0], 1, 4),
     ("tiled128", "tiled", 350, 256, 512, [129, 0, 128, 127, 1, 0, 200, 115], 1, 4),
-    # >= 256 rows per expert on average: 384-token tiles in the down projection,
-    # >= 1024: in the gate-up projection too (segments of 1, 384, 385 and > 1024 rows)
-    ("tiled_down384", "tiled", 1200, 384, 256, [500, 0, 385, 383, 1, 0, 700, 400], 0, 1),
-    ("tiled384", "tiled", 4096, 256, 384, [0, 1500, 1, 384, 769, 0, 2000, 3000], 0, 1),
-    ("tiled384_partials2", "tiled", 4096, 256, 512, [0, 1500, 1, 384, 769, 0, 2000, 3000], 1, 2),
-    ("tiled384_partials4", "tiled", 4096, 256, 1024, [3000, 1, 0, 385, 0, 1500, 2000, 769], 1, 4),
+    # many rows per expert: several 256-token tiles per segment (segments of 1, 255,
+    # 256, 257 and > 1024 rows), 1, 2 and 4 partial sums
+    ("tiled_many_rows", "tiled", 1200, 384, 256, [500, 0, 257, 255, 1, 0, 700, 256], 0, 1),
+    ("tiled_long_segments", "tiled", 4096, 256, 384, [0, 1500, 1, 384, 769, 0, 2000, 3000], 0, 1),
+    ("tiled_partials2", "tiled", 4096, 2048, 512, [0, 1500, 1, 256, 769, 0, 2000, 3000], 1, 2),
+    ("tiled_partials4_long", "tiled", 4096, 256, 1024, [3000, 1, 0, 257, 0, 1500, 2000, 769], 1, 4),
 ]
 
 
