@@ -113,7 +113,7 @@ int64_t rows_per_expert(const moe_problem *p) { return (p->T * p->K + p->E - 1) 
 
 int gate_up_tile(const moe_problem *p) {
   const int64_t n = rows_per_expert(p);
-  return n <= 64 ? 64 : n <= 96 ? 128 : 256;
+  return n <= 48 ? 64 : n <= 96 ? 128 : 256;
 }
 int down_tile(const moe_problem *p) {
   const int64_t n = rows_per_expert(p);

@@ -307,13 +307,18 @@ __global__ __launch_bounds__(512) void tiled256_kernel(const uint16_t *__restric
 // from HBM once and the matrix work is mostly padding, so the tile narrows to
 // BT = 64 or 128 tokens (256 weight rows as before). 8 wavefronts in a 4 x 2
 // grid, each 64 weight rows x BT/2 tokens (2 x BT/64 accumulators); for gate-up
-// a wavefront's 64 rows are 32 W1 and the same 32 W3 rows. BT = 64 needs 80 KiB
-// of LDS, so two workgroups share a compute unit and keep more bytes in flight.
+// a wavefront's 64 rows are 32 W1 and the same 32 W3 rows. BT = 64 uses two
+// stages of both tiles (80 KiB of LDS), so two workgroups share a compute unit
+// and keep more bytes in flight; BT = 128 has room for a third weight stage
+// (128 KiB) and fetches the weights two k-blocks ahead, as tiled256_kernel.
+// The kernels below own the LDS (separate arrays per slot, so that the compiler
+// sees the copies in flight cannot alias the slot being read) and run this body.
 template <bool GATEUP, int BT>
-__global__ __launch_bounds__(512) void tiled_small_kernel(
+__device__ __forceinline__ void small_body(
     const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
     const uint16_t *__restrict__ Wa, const uint16_t *__restrict__ Wb, void *__restrict__ out,
-    int N, int K, int ksplit, int64_t part_stride) {
+    int N, int K, int ksplit, int64_t part_stride, uint16_t *sW0, uint16_t *sW1, uint16_t *sW2,
+    uint16_t *sX0, uint16_t *sX1) {
   constexpr int NT = BT / 64;  // 32-token accumulator columns per wavefront
   constexpr int XI = BT / 64;  // token-row DMA instructions per wavefront
   Tile tl;
@@ -324,11 +329,6 @@ __global__ __launch_bounds__(512) void tiled_small_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-
-  __shared__ __attribute__((aligned(1024))) uint16_t sW0[256 * 64];
-  __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
-  __shared__ __attribute__((aligned(1024))) uint16_t sX0[BT * 64];
-  __shared__ __attribute__((aligned(1024))) uint16_t sX1[BT * 64];
 
   // ---- DMA assignment as in tiled_kernel: wave w fills weight rows
   // [32w, 32w+32) (for gate-up: W1 rows if w is even, else the W3 rows of the
@@ -378,11 +378,15 @@ __global__ __launch_bounds__(512) void tiled_small_kernel(
   const int nk = K / 64 / ksplit;  // k-blocks of this part (an even count)
   const int kb0 = ks * nk;
 
-#define DMA(SW, SX, KB)                                                                    \
+#define DMAW(SW, KB)                                                                       \
   {                                                                                        \
     const uint32_t k0 = uint32_t((kb0 + min(KB, nk - 1)) * 64);                            \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
       dma16(wmat + wofs[i] + k0, (lds_void *)(SW + (dma_row + i * 8) * 64));              \
+  }
+#define DMAX(SX, KB)                                                                       \
+  {                                                                                        \
+    const uint32_t k0 = uint32_t((kb0 + min(KB, nk - 1)) * 64);                            \
     _Pragma("unroll") for (int i = 0; i < XI; ++i)                                         \
       dma16(x_t + xofs[i] + k0, (lds_void *)(SX + (dma_xrow + i * 8) * 64));              \
   }
@@ -414,20 +418,59 @@ __global__ __launch_bounds__(512) void tiled_small_kernel(
     }                                                                                      \
   }
 
-  DMA(sW0, sX0, 0)
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    DMA(sW1, sX1, kt + 1)
-    COMPUTE(sW0, sX0)
+  if constexpr (BT == 64) {
+    DMAW(sW0, 0)
+    DMAX(sX0, 0)
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    DMA(sW0, sX0, kt + 2)
-    COMPUTE(sW1, sX1)
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      DMAW(sW1, kt + 1)
+      DMAX(sX1, kt + 1)
+      COMPUTE(sW0, sX0)
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      DMAW(sW0, kt + 2)
+      DMAX(sX0, kt + 2)
+      COMPUTE(sW1, sX1)
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+    }
+  } else {
+    // as tiled256_kernel: tokens one k-block ahead, weights two
+#define STEP(KB, WS, XS, XN, WN)                                                           \
+  DMAX(sX##XN, (KB) + 1)                                                                   \
+  DMAW(sW##WN, (KB) + 2)                                                                   \
+  COMPUTE(sW##WS, sX##XS)                                                                  \
+  __builtin_amdgcn_s_waitcnt(kWaitVm4);                                                    \
+  TILED_BARRIER()
+    DMAW(sW0, 0)
+    DMAX(sX0, 0)
+    DMAW(sW1, 1)
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    TILED_BARRIER()
+    int kt = 0;
+    for (; kt + 6 <= nk; kt += 6) {
+      STEP(kt + 0, 0, 0, 1, 2)
+      STEP(kt + 1, 1, 1, 0, 0)
+      STEP(kt + 2, 2, 0, 1, 1)
+      STEP(kt + 3, 0, 1, 0, 2)
+      STEP(kt + 4, 1, 0, 1, 0)
+      STEP(kt + 5, 2, 1, 0, 1)
+    }
+    if (kt < nk) {
+      STEP(kt + 0, 0, 0, 1, 2)
+      STEP(kt + 1, 1, 1, 0, 0)
+      kt += 2;
+    }
+    if (kt < nk) {
+      STEP(kt + 0, 2, 0, 1, 1)
+      STEP(kt + 1, 0, 1, 0, 2)
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no copy in flight past the main loop
+#undef STEP
   }
-#undef DMA
+#undef DMAW
+#undef DMAX
 #undef COMPUTE
 
   // ---- epilogue (fragment layout as in tiled_kernel)
@@ -466,6 +509,33 @@ __global__ __launch_bounds__(512) void tiled_small_kernel(
   }
 }
 
+template <bool GATEUP>
+__global__ __launch_bounds__(512) void tiled64_kernel(
+    const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
+    const uint16_t *__restrict__ Wa, const uint16_t *__restrict__ Wb, void *__restrict__ out,
+    int N, int K, int ksplit, int64_t part_stride) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sW0[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX0[64 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX1[64 * 64];
+  small_body<GATEUP, 64>(X, offsets, E, Wa, Wb, out, N, K, ksplit, part_stride, sW0, sW1,
+                         nullptr, sX0, sX1);
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(512) void tiled128_kernel(
+    const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
+    const uint16_t *__restrict__ Wa, const uint16_t *__restrict__ Wb, void *__restrict__ out,
+    int N, int K, int ksplit, int64_t part_stride) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sW0[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW2[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX0[128 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX1[128 * 64];
+  small_body<GATEUP, 128>(X, offsets, E, Wa, Wb, out, N, K, ksplit, part_stride, sW0, sW1, sW2,
+                          sX0, sX1);
+}
+
 // Upper bound of the tile count for any split of S rows over E experts.
 inline unsigned tiled_grid(int64_t S, int E, int N, int cols, int bt, int ksplit) {
   const int64_t ct = (N + cols - 1) / cols;
@@ -482,11 +552,11 @@ void launch_bt(int bt, const void *x, const int32_t *offsets, const void *wa, co
   const auto *ap = static_cast<const uint16_t *>(wa);
   const auto *bp = static_cast<const uint16_t *>(wb);
   if (bt == 128)
-    hipLaunchKernelGGL((tiled_small_kernel<GATEUP, 128>), grid, dim3(512), 0, s, xp, offsets, E,
-                       ap, bp, out, N, K, ksplit, part_stride);
+    hipLaunchKernelGGL((tiled128_kernel<GATEUP>), grid, dim3(512), 0, s, xp, offsets, E, ap, bp,
+                       out, N, K, ksplit, part_stride);
   else if (bt == 64)
-    hipLaunchKernelGGL((tiled_small_kernel<GATEUP, 64>), grid, dim3(512), 0, s, xp, offsets, E,
-                       ap, bp, out, N, K, ksplit, part_stride);
+    hipLaunchKernelGGL((tiled64_kernel<GATEUP>), grid, dim3(512), 0, s, xp, offsets, E, ap, bp,
+                       out, N, K, ksplit, part_stride);
   else
     hipLaunchKernelGGL((tiled256_kernel<GATEUP>), grid, dim3(512), 0, s, xp, offsets, E, ap, bp,
                        out, N, K, ksplit, part_stride);
