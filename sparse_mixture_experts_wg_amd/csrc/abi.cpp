@@ -68,10 +68,15 @@ moe_status check_problem(const moe_problem *p) {
   if (p->reserved != 0) return fail(MOE_ERR_UNSUPPORTED, "reserved field must be 0");
   if (p->flags & ~MOE_FLAG_DOWN_PARTIALS)
     return fail(MOE_ERR_UNSUPPORTED, "flags=0x%x: unknown bits", unsigned(p->flags));
-  // tiled grid: column blocks x (token blocks + E) must fit a 1-D grid
+  // tiled grids: column blocks x (token blocks + E) (x 4 partial sums for the
+  // down projection) must fit a 1-D grid and 32-bit tile arithmetic; a batch
+  // with more than 96 rows per expert uses 256-token blocks, a smaller one has
+  // few blocks anyway
   const int64_t S = p->T * p->K;
-  const int64_t tiles = (p->h / 128) * ((S + 255) / 256 + p->E);
-  if (tiles > kMaxIndex / 2) return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch");
+  const int64_t tiles_gu = (p->h / 128) * ((S + 255) / 256 + p->E);
+  const int64_t tiles_dn = 4 * ((p->d + 255) / 256) * ((S + 255) / 256 + p->E);
+  if (tiles_gu > kMaxIndex / 2 || tiles_dn > kMaxIndex / 2)
+    return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch");
   // stream grid: S / 32 row groups in the z dimension
   if (p->dtype == MOE_BF16 && resolve(p) == MOE_PATH_STREAM && (S + 31) / 32 >= (int64_t(1) << 16))
     return fail(MOE_ERR_UNSUPPORTED, "T=%lld too large for the STREAM path (use TILED)",
