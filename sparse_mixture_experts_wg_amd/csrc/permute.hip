@@ -11,7 +11,12 @@
 // over the 16 wavefront totals gives every thread its first row per expert,
 // and a second pass over the same range assigns rows in slot order. The result
 // is the stable order (ascending s = t*K + k within an expert) with no atomics.
-// The slot index arrays are small (S int32), so one CU suffices.
+// The slot index arrays are small (S int32), so one CU suffices. From 2048 up
+// to 32768 slots the expert ids are first copied into LDS with coalesced 16-byte loads
+// and the slot positions are collected there and written back coalesced (each
+// thread's contiguous slot range would otherwise make every wavefront access
+// touch 64 separate lines); up to 16384 slots the sorted-row -> token map is
+// assembled in LDS too instead of being scattered to global memory.
 // With a capacity C (the capacity variant) a slot whose rank within its expert
 // is C or more is dropped (slot_pos -1, no row) and the offsets count the kept
 // rows min(n_e, C) only.
@@ -25,6 +30,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWavesPerBlock = kThreads / 64;
+constexpr int kStage = 32768;  // slots staged in LDS (128 KiB)
 
 __global__ __launch_bounds__(kThreads) void permute_index_kernel(
     const int32_t *__restrict__ idx, int64_t S, int K, int E, int capacity,
@@ -33,18 +39,32 @@ __global__ __launch_bounds__(kThreads) void permute_index_kernel(
   __shared__ int32_t wave_tot[kWavesPerBlock][8];
   __shared__ int32_t wave_pre[kWavesPerBlock][8];
   __shared__ int32_t expert_off[9];
+  // expert ids, then slot positions (S <= kStage); with S <= kStage / 2 the
+  // second half holds the sorted-row -> token map
+  __shared__ int32_t sidx[kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t chunk = (S + kThreads - 1) / kThreads;
   const int64_t s0 = min(S, int64_t(tid) * chunk);
   const int64_t s1 = min(S, s0 + chunk);
+  // (small batches skip the staging: a few slots per thread gain nothing from it)
+  const bool staged = S >= 2048 && S <= kStage;
+  const bool staged_perm = staged && S <= kStage / 2;
+  int32_t *sperm = sidx + kStage / 2;
+  if (staged) {
+    const int64_t S4 = S & ~int64_t(3);
+    for (int64_t i = int64_t(tid) * 4; i < S4; i += 4 * kThreads)
+      *reinterpret_cast<int4 *>(sidx + i) = *reinterpret_cast<const int4 *>(idx + i);
+    for (int64_t i = S4 + tid; i < S; i += kThreads) sidx[i] = idx[i];
+    __syncthreads();
+  }
 
   int cnt[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) cnt[e] = 0;
   for (int64_t s = s0; s < s1; ++s) {
-    const int e = idx[s];
+    const int e = staged ? sidx[s] : idx[s];
 #pragma unroll
     for (int q = 0; q < 8; ++q) cnt[q] += (q == e && q < E) ? 1 : 0;
   }
@@ -92,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void permute_index_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) rank[e] = wave_pre[wave][e] + incl[e] - cnt[e];
   for (int64_t s = s0; s < s1; ++s) {
-    const int e = idx[s];
+    const int e = staged ? sidx[s] : idx[s];
     int p = -1;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -101,8 +121,31 @@ __global__ __launch_bounds__(kThreads) void permute_index_kernel(
         rank[q] += 1;
       }
     }
-    slot_pos[s] = p;
-    if (p >= 0) perm_token[p] = int32_t(s / K);
+    if (staged)
+      sidx[s] = p;  // this thread's own slot: no other thread reads it
+    else
+      slot_pos[s] = p;
+    if (p >= 0) {
+      if (staged_perm)
+        sperm[p] = int32_t(s / K);
+      else
+        perm_token[p] = int32_t(s / K);
+    }
+  }
+  if (staged) {
+    __syncthreads();
+    const int64_t S4 = S & ~int64_t(3);
+    for (int64_t i = int64_t(tid) * 4; i < S4; i += 4 * kThreads)
+      *reinterpret_cast<int4 *>(slot_pos + i) = *reinterpret_cast<const int4 *>(sidx + i);
+    for (int64_t i = S4 + tid; i < S; i += kThreads) slot_pos[i] = sidx[i];
+    if (staged_perm) {
+      // rows [0, offsets[E]) exist; the rest of perm_token is left as it was
+      const int64_t R = expert_off[E];
+      const int64_t R4 = R & ~int64_t(3);
+      for (int64_t i = int64_t(tid) * 4; i < R4; i += 4 * kThreads)
+        *reinterpret_cast<int4 *>(perm_token + i) = *reinterpret_cast<const int4 *>(sperm + i);
+      for (int64_t i = R4 + tid; i < R; i += kThreads) perm_token[i] = sperm[i];
+    }
   }
 }
 
