@@ -213,7 +213,7 @@ moe_status do_permute(const moe_problem *p, const void *x, const int32_t *idx, i
                     "gather launch");
 }
 
-// rowmap (nullable, STREAM path only): sorted row r is row rowmap[r] of x_perm.
+// rowmap (nullable, bf16 only): sorted row r is row rowmap[r] of x_perm.
 moe_status do_gate_up(const moe_problem *p, const void *x_perm, const int32_t *offsets,
                       const void *w1, const void *w3, void *act, hipStream_t s,
                       const int32_t *rowmap = nullptr) {
@@ -227,8 +227,8 @@ moe_status do_gate_up(const moe_problem *p, const void *x_perm, const int32_t *o
     e = moe::launch_stream_gate_up(x_perm, rowmap, offsets, w1, w3, act, p->E, int(p->d),
                                    int(p->h), p->T, S, s);
   else
-    e = moe::launch_tiled_gate_up(x_perm, offsets, w1, w3, act, p->E, S, int(p->d), int(p->h),
-                                  gate_up_tile(p), s);
+    e = moe::launch_tiled_gate_up(x_perm, rowmap, offsets, w1, w3, act, p->E, S, int(p->d),
+                                  int(p->h), gate_up_tile(p), s);
   return hip_result(e, "gate-up launch");
 }
 
@@ -301,8 +301,8 @@ moe_status run_layer(const moe_problem *p, const void *x, const void *w_g, const
   float *o_perm = reinterpret_cast<float *>(base + L.o_perm);
   const hipStream_t s = as_stream(stream);
   CHECK(do_route(p, x, w_g, idx, w, nullptr, s));
-  if (p->dtype == MOE_BF16 && resolve(p) == MOE_PATH_STREAM) {
-    // the streaming gate-up reads each token row of x through perm_token, so
+  if (p->dtype == MOE_BF16) {
+    // the bf16 gate-up kernels read each token row of x through perm_token, so
     // the layer needs no gathered copy of x
     CHECK(do_permute(p, x, idx, offsets, perm, slot, nullptr, s));
     CHECK(do_gate_up(p, x, offsets, w1, w3, act, s, perm));

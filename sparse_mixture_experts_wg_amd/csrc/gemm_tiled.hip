@@ -162,7 +162,8 @@ __global__ __launch_bounds__(512) void tiled256_kernel(const uint16_t *__restric
                                                        const uint16_t *__restrict__ Wa,
                                                        const uint16_t *__restrict__ Wb,
                                                        void *__restrict__ out, int N, int K,
-                                                       int ksplit, int64_t part_stride) {
+                                                       int ksplit, int64_t part_stride,
+                                                       const int32_t *__restrict__ rowmap) {
   constexpr int BT = 256;
   Tile tl;
   if (!find_tile<BT, GATEUP ? 128 : 256>(offsets, E, N, ksplit, tl)) return;
@@ -185,8 +186,10 @@ __global__ __launch_bounds__(512) void tiled256_kernel(const uint16_t *__restric
   const size_t mat_elems = size_t(N) * K;
   const uint16_t *wmat = Wa + size_t(tl.e) * mat_elems;
   if (GATEUP && ((wave >> 1) & 1)) wmat = Wb + size_t(tl.e) * mat_elems;
-  const uint16_t *x_t = X + size_t(tl.row0 + tl.m0) * K;
-  uint32_t wofs[4], xofs[4];
+  // token rows: x_perm rows row0 + m0 + r, or with a row map the rows
+  // rowmap[...] of the unsorted input (one pointer per DMA instruction)
+  uint32_t wofs[4];
+  const uint16_t *xsrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 32 + i * 8 + (lane >> 3);
@@ -195,7 +198,8 @@ __global__ __launch_bounds__(512) void tiled256_kernel(const uint16_t *__restric
     if constexpr (GATEUP) wrow = tl.c0 + ((r >> 7) << 6) + (r & 63);
     else wrow = min(tl.c0 + r, N - 1);
     wofs[i] = uint32_t(wrow) * uint32_t(K) + c * 8;
-    xofs[i] = uint32_t(min(r, tl.ne - 1 - tl.m0)) * uint32_t(K) + c * 8;
+    const int xr = tl.row0 + tl.m0 + min(r, tl.ne - 1 - tl.m0);
+    xsrc[i] = X + size_t(rowmap ? rowmap[xr] : xr) * K + c * 8;
   }
   const int dma_row = wave * 32;
 
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(512) void tiled256_kernel(const uint16_t *__restric
   {                                                                                        \
     const uint32_t k0 = uint32_t((kb0 + min(KB, nk - 1)) * 64);                            \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
-      dma16(x_t + xofs[i] + k0, (lds_void *)(SX + (dma_row + i * 8) * 64));                \
+      dma16(xsrc[i] + k0, (lds_void *)(SX + (dma_row + i * 8) * 64));                      \
   }
   // both fragment sets double-buffered: the next kk's six reads are issued
   // ahead of the current kk's eight MFMAs
@@ -317,8 +321,8 @@ template <bool GATEUP, int BT>
 __device__ __forceinline__ void small_body(
     const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
     const uint16_t *__restrict__ Wa, const uint16_t *__restrict__ Wb, void *__restrict__ out,
-    int N, int K, int ksplit, int64_t part_stride, uint16_t *sW0, uint16_t *sW1, uint16_t *sW2,
-    uint16_t *sX0, uint16_t *sX1) {
+    int N, int K, int ksplit, int64_t part_stride, const int32_t *__restrict__ rowmap,
+    uint16_t *sW0, uint16_t *sW1, uint16_t *sW2, uint16_t *sX0, uint16_t *sX1) {
   constexpr int NT = BT / 64;  // 32-token accumulator columns per wavefront
   constexpr int XI = BT / 64;  // token-row DMA instructions per wavefront
   Tile tl;
@@ -336,11 +340,11 @@ __device__ __forceinline__ void small_body(
   const size_t mat_elems = size_t(N) * K;
   const uint16_t *wmat = Wa + size_t(e) * mat_elems;
   if (GATEUP && (wave & 1)) wmat = Wb + size_t(e) * mat_elems;
-  const uint16_t *x_t = X + size_t(row0 + m0) * K;
   const int xlim = ne - 1 - m0;
   const int dma_row = wave * 32;
   const int dma_xrow = wave * (BT / 8);
-  uint32_t wofs[4], xofs[XI];
+  uint32_t wofs[4];
+  const uint16_t *xsrc[XI];  // token rows (through the row map if given)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int lr = lane >> 3;
@@ -354,8 +358,8 @@ __device__ __forceinline__ void small_body(
   for (int i = 0; i < XI; ++i) {
     const int lr = lane >> 3;
     const int q = (dma_xrow / 8 + i) & 3;
-    xofs[i] = uint32_t(min(dma_xrow + 8 * i + lr, xlim)) * uint32_t(K) +
-              (((lane & 7) ^ lr ^ q) << 3);
+    const int xr = row0 + m0 + min(dma_xrow + 8 * i + lr, xlim);
+    xsrc[i] = X + size_t(rowmap ? rowmap[xr] : xr) * K + (((lane & 7) ^ lr ^ q) << 3);
   }
 
   // ---- fragment read addresses (bytes): row (lane & 31) of a 32-row group,
@@ -388,7 +392,7 @@ __device__ __forceinline__ void small_body(
   {                                                                                        \
     const uint32_t k0 = uint32_t((kb0 + min(KB, nk - 1)) * 64);                            \
     _Pragma("unroll") for (int i = 0; i < XI; ++i)                                         \
-      dma16(x_t + xofs[i] + k0, (lds_void *)(SX + (dma_xrow + i * 8) * 64));              \
+      dma16(xsrc[i] + k0, (lds_void *)(SX + (dma_xrow + i * 8) * 64));                    \
   }
 #define COMPUTE(SW, SX)                                                                    \
   {                                                                                        \
@@ -513,27 +517,27 @@ template <bool GATEUP>
 __global__ __launch_bounds__(512) void tiled64_kernel(
     const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
     const uint16_t *__restrict__ Wa, const uint16_t *__restrict__ Wb, void *__restrict__ out,
-    int N, int K, int ksplit, int64_t part_stride) {
+    int N, int K, int ksplit, int64_t part_stride, const int32_t *__restrict__ rowmap) {
   __shared__ __attribute__((aligned(1024))) uint16_t sW0[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX0[64 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX1[64 * 64];
-  small_body<GATEUP, 64>(X, offsets, E, Wa, Wb, out, N, K, ksplit, part_stride, sW0, sW1,
-                         nullptr, sX0, sX1);
+  small_body<GATEUP, 64>(X, offsets, E, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0,
+                         sW1, nullptr, sX0, sX1);
 }
 
 template <bool GATEUP>
 __global__ __launch_bounds__(512) void tiled128_kernel(
     const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
     const uint16_t *__restrict__ Wa, const uint16_t *__restrict__ Wb, void *__restrict__ out,
-    int N, int K, int ksplit, int64_t part_stride) {
+    int N, int K, int ksplit, int64_t part_stride, const int32_t *__restrict__ rowmap) {
   __shared__ __attribute__((aligned(1024))) uint16_t sW0[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sW2[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX0[128 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX1[128 * 64];
-  small_body<GATEUP, 128>(X, offsets, E, Wa, Wb, out, N, K, ksplit, part_stride, sW0, sW1, sW2,
-                          sX0, sX1);
+  small_body<GATEUP, 128>(X, offsets, E, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0,
+                          sW1, sW2, sX0, sX1);
 }
 
 // Upper bound of the tile count for any split of S rows over E experts.
@@ -544,37 +548,37 @@ inline unsigned tiled_grid(int64_t S, int E, int N, int cols, int bt, int ksplit
 }
 
 template <bool GATEUP>
-void launch_bt(int bt, const void *x, const int32_t *offsets, const void *wa, const void *wb,
-               void *out, int E, int64_t S, int N, int K, int ksplit, int64_t part_stride,
-               hipStream_t s) {
+void launch_bt(int bt, const void *x, const int32_t *rowmap, const int32_t *offsets,
+               const void *wa, const void *wb, void *out, int E, int64_t S, int N, int K,
+               int ksplit, int64_t part_stride, hipStream_t s) {
   const dim3 grid(tiled_grid(S, E, N, GATEUP ? 128 : 256, bt, ksplit));
   const auto *xp = static_cast<const uint16_t *>(x);
   const auto *ap = static_cast<const uint16_t *>(wa);
   const auto *bp = static_cast<const uint16_t *>(wb);
   if (bt == 128)
     hipLaunchKernelGGL((tiled128_kernel<GATEUP>), grid, dim3(512), 0, s, xp, offsets, E, ap, bp,
-                       out, N, K, ksplit, part_stride);
+                       out, N, K, ksplit, part_stride, rowmap);
   else if (bt == 64)
     hipLaunchKernelGGL((tiled64_kernel<GATEUP>), grid, dim3(512), 0, s, xp, offsets, E, ap, bp,
-                       out, N, K, ksplit, part_stride);
+                       out, N, K, ksplit, part_stride, rowmap);
   else
     hipLaunchKernelGGL((tiled256_kernel<GATEUP>), grid, dim3(512), 0, s, xp, offsets, E, ap, bp,
-                       out, N, K, ksplit, part_stride);
+                       out, N, K, ksplit, part_stride, rowmap);
 }
 
 }  // namespace
 
-hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
-                                const void *w3, void *act, int E, int64_t S, int d, int h,
-                                int bt, hipStream_t s) {
-  launch_bt<true>(bt, x_perm, offsets, w1, w3, act, E, S, h, d, 1, 0, s);
+hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *rowmap, const int32_t *offsets,
+                                const void *w1, const void *w3, void *act, int E, int64_t S,
+                                int d, int h, int bt, hipStream_t s) {
+  launch_bt<true>(bt, x_perm, rowmap, offsets, w1, w3, act, E, S, h, d, 1, 0, s);
   return hipGetLastError();
 }
 
 hipError_t launch_tiled_down(const void *act, const int32_t *offsets, const void *w2,
                              float *o_perm, int E, int64_t S, int d, int h, int bt, int parts,
                              hipStream_t s) {
-  launch_bt<false>(bt, act, offsets, w2, nullptr, o_perm, E, S, d, h, parts, S * d, s);
+  launch_bt<false>(bt, act, nullptr, offsets, w2, nullptr, o_perm, E, S, d, h, parts, S * d, s);
   return hipGetLastError();
 }
 

@@ -55,10 +55,11 @@ hipError_t launch_stream_gate_up(const void *x_perm, const int32_t *rowmap,
 hipError_t launch_stream_down(const void *act, const int32_t *offsets, const void *w2,
                               float *o_perm, int E, int d, int h, int64_t rows_hint,
                               int64_t rows_bound, hipStream_t s);
-// TILED path (bf16 matrix cores); bt: token tile, 64, 128 or 256.
-hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *offsets, const void *w1,
-                                const void *w3, void *act, int E, int64_t S, int d, int h,
-                                int bt, hipStream_t s);
+// TILED path (bf16 matrix cores); bt: token tile, 64, 128 or 256; rowmap as
+// for the streaming gate-up.
+hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *rowmap, const int32_t *offsets,
+                                const void *w1, const void *w3, void *act, int E, int64_t S,
+                                int d, int h, int bt, hipStream_t s);
 // parts (1, 2 or 4; needs h % (128 * parts) == 0): partial sums over h, part q
 // at o_perm + q * S * d.
 hipError_t launch_tiled_down(const void *act, const int32_t *offsets, const void *w2,
