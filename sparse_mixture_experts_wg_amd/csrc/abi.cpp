@@ -285,10 +285,19 @@ moe_status check_layer_args(const void *w_g, const void *w1, const void *w3, con
   return MOE_OK;
 }
 
-// The whole layer on checked arguments; `residual` (nullable) is added to y.
+// The pre-norm block's input: x = RMSNorm(h) * g is written to `x` by the
+// router's own kernel.
+struct NormIn {
+  const void *h, *g;
+  float eps;
+};
+
+// The whole layer on checked arguments; `residual` (nullable) is added to y;
+// with `norm`, x is first computed from norm->h (fused into the route step).
 moe_status run_layer(const moe_problem *p, const void *x, const void *w_g, const void *w1,
                      const void *w3, const void *w2, const void *residual, void *y,
-                     int32_t *topk_idx, float *topk_w, void *ws, void *stream) {
+                     int32_t *topk_idx, float *topk_w, void *ws, void *stream,
+                     const NormIn *norm = nullptr) {
   const ForwardLayout L = forward_layout(p);
   char *base = static_cast<char *>(ws);
   int32_t *idx = topk_idx ? topk_idx : reinterpret_cast<int32_t *>(base + L.idx);
@@ -300,7 +309,13 @@ moe_status run_layer(const moe_problem *p, const void *x, const void *w_g, const
   void *act = base + L.act;
   float *o_perm = reinterpret_cast<float *>(base + L.o_perm);
   const hipStream_t s = as_stream(stream);
-  CHECK(do_route(p, x, w_g, idx, w, nullptr, s));
+  if (norm)
+    CHECK(hip_result(moe::launch_norm_route(p->dtype == MOE_BF16, norm->h, norm->g, norm->eps, w_g,
+                                            p->T, int(p->d), p->E, p->K, const_cast<void *>(x),
+                                            idx, w, s),
+                     "rmsnorm+route launch"));
+  else
+    CHECK(do_route(p, x, w_g, idx, w, nullptr, s));
   if (p->dtype == MOE_BF16) {
     // the bf16 gate-up kernels read each token row of x through perm_token, so
     // the layer needs no gathered copy of x
@@ -511,8 +526,8 @@ moe_status moe_block_forward(const moe_problem *p, const void *h, const void *no
       return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
     // the normalised input x lives after the layer's own workspace
     void *x = static_cast<char *>(ws) + forward_layout(p).total;
-    CHECK(do_rmsnorm(p, h, norm_w, eps, x, as_stream(stream)));
-    return run_layer(p, x, w_g, w1, w3, w2, h, y, topk_idx, topk_w, ws, stream);
+    const NormIn norm{h, norm_w, eps};
+    return run_layer(p, x, w_g, w1, w3, w2, h, y, topk_idx, topk_w, ws, stream, &norm);
   });
 }
 

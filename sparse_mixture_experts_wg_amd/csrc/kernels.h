@@ -32,6 +32,13 @@ hipError_t launch_rmsnorm(bool bf16, const void *h, const void *g, float eps, in
 hipError_t launch_route(bool bf16, const void *x, const void *wg, int64_t T, int d, int E, int K,
                         int32_t *idx, float *w, float *logits, hipStream_t s);
 
+// RMSNorm of the block input fused in front of the router: writes x (as
+// launch_rmsnorm) and routes it (as launch_route, no logits); bitwise the same
+// as the two launches.
+hipError_t launch_norm_route(bool bf16, const void *h, const void *g, float eps, const void *wg,
+                             int64_t T, int d, int E, int K, void *x, int32_t *idx, float *w,
+                             hipStream_t s);
+
 // ---- permute ----------------------------------------------------------------
 // capacity > 0: each expert keeps its `capacity` earliest slots, later ones get
 // slot_pos -1 and no row.

@@ -63,6 +63,44 @@ __device__ __forceinline__ void load_wrow(const void *wg, int64_t j, int E, floa
   }
 }
 
+// Top-K of one token's logits l[e] = total[t * 8 + e]: by (logit desc, index
+// asc), values tracked beside indices so that no register array is indexed at
+// run time; then the softmax over the kept logits.
+__device__ __forceinline__ void topk_out(const float *total, int t, int64_t tok, int E, int K,
+                                         int32_t *__restrict__ idx, float *__restrict__ w,
+                                         float *__restrict__ logits) {
+  float l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) l[e] = total[t * 8 + e];
+  int b0 = 0;
+  float v0 = l[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e)
+    if (e < E && l[e] > v0) { v0 = l[e]; b0 = e; }
+  if (K == 1) {
+    idx[tok] = b0;
+    w[tok] = 1.0f;
+  } else {
+    int b1 = -1;
+    float v1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < E && e != b0 && (b1 < 0 || l[e] > v1)) { v1 = l[e]; b1 = e; }
+    // softmax over the two kept logits, v1 <= v0
+    const float r = expf(v1 - v0);
+    const float w0 = 1.0f / (1.0f + r);
+    idx[tok * 2] = b0;
+    idx[tok * 2 + 1] = b1;
+    w[tok * 2] = w0;
+    w[tok * 2 + 1] = r * w0;
+  }
+  if (logits) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < E) logits[tok * E + e] = l[e];
+  }
+}
+
 template <bool BF16, bool E8, int kTPB>
 __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ x,
                                                     const void *__restrict__ wg, int64_t T, int d,
@@ -118,39 +156,117 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ x,
   __syncthreads();
   const int t = threadIdx.x;
   if (t >= ntok) return;
-  const int64_t tok = tok0 + t;
-  float l[8];
+  topk_out(total, t, tok0 + t, E, K, idx, w, logits);
+}
+
+// The pre-norm block's RMSNorm fused in front of the router: x = RMSNorm(h) * g
+// is computed, written (the expert path reads it) and routed in one pass. The
+// mean square of each token follows norm.hip's order exactly (thread i sums the
+// squares of chunks i, i + 256, ... in order, a butterfly per wavefront, the 4
+// wavefront sums added 0+1+2+3), and the logits follow route_kernel's order on
+// the rounded x, so x, the logits and the routing are bitwise those of the two
+// separate kernels.
+template <bool BF16>
+__device__ __forceinline__ void store8(void *base, int64_t elem, const float v[8]) {
+  if constexpr (BF16) {
+    u32x4 q;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) l[e] = total[t * 8 + e];
-  // top-1 / top-2 by (logit desc, index asc); values tracked beside indices so
-  // that no register array is indexed at run time
-  int b0 = 0;
-  float v0 = l[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e)
-    if (e < E && l[e] > v0) { v0 = l[e]; b0 = e; }
-  if (K == 1) {
-    idx[tok] = b0;
-    w[tok] = 1.0f;
+    for (int i = 0; i < 4; ++i) q[i] = f32_to_bf16_bits(v[2 * i]) | (f32_to_bf16_bits(v[2 * i + 1]) << 16);
+    *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(base) + elem) = q;
   } else {
-    int b1 = -1;
-    float v1 = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (e < E && e != b0 && (b1 < 0 || l[e] > v1)) { v1 = l[e]; b1 = e; }
-    // softmax over the two kept logits, v1 <= v0
-    const float r = expf(v1 - v0);
-    const float w0 = 1.0f / (1.0f + r);
-    idx[tok * 2] = b0;
-    idx[tok * 2 + 1] = b1;
-    w[tok * 2] = w0;
-    w[tok * 2 + 1] = r * w0;
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + elem) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + elem + 4) = f32x4{v[4], v[5], v[6], v[7]};
   }
-  if (logits) {
+}
+
+template <bool BF16, bool E8, int kTPB>
+__global__ __launch_bounds__(256) void norm_route_kernel(
+    const void *__restrict__ h, const void *__restrict__ g, float eps,
+    const void *__restrict__ wg, int64_t T, int d, int E, int K, void *__restrict__ x,
+    int32_t *__restrict__ idx, float *__restrict__ w, float *__restrict__ logits) {
+  __shared__ float part[kWaves][64];
+  __shared__ float total[64];
+  __shared__ float ssp[kTPB][kWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t tok0 = int64_t(blockIdx.x) * kTPB;
+  const int ntok = int(min(int64_t(kTPB), T - tok0));
+  const int chunks = d >> 3;
+
+  // mean square per token, in norm.hip's order
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (e < E) logits[tok * E + e] = l[e];
+  for (int t = 0; t < kTPB; ++t) {
+    if (t >= ntok) continue;
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+      float v[8];
+      load8<BF16>(h, (tok0 + t) * d + int64_t(c) * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    if (lane == 0) ssp[t][wave] = ss;
   }
+  __syncthreads();
+  float inv[kTPB];
+#pragma unroll
+  for (int t = 0; t < kTPB; ++t) {
+    const float ms = (((ssp[t][0] + ssp[t][1]) + ssp[t][2]) + ssp[t][3]) / float(d);
+    inv[t] = 1.0f / sqrtf(ms + eps);
+  }
+
+  float acc[kTPB][8];
+#pragma unroll
+  for (int t = 0; t < kTPB; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
+
+  const int quarter = d >> 5;
+  const int cbeg = wave * quarter, cend = cbeg + quarter;
+#pragma unroll 2
+  for (int c = cbeg + lane; c < cend; c += 64) {
+    float wv[8][8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) load_wrow<BF16, E8>(wg, int64_t(c) * 8 + r, E, wv[r]);
+    float gv[8];
+    load8<BF16>(g, int64_t(c) * 8, gv);
+#pragma unroll
+    for (int t = 0; t < kTPB; ++t) {
+      if (t >= ntok) continue;
+      float xv[8];
+      load8<BF16>(h, (tok0 + t) * d + int64_t(c) * 8, xv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xv[i] = (xv[i] * inv[t]) * gv[i];
+      store8<BF16>(x, (tok0 + t) * d + int64_t(c) * 8, xv);
+      if constexpr (BF16) {  // route on x as stored: rounded once to bf16
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xv[i] = bf16_bits_to_f32(f32_to_bf16_bits(xv[i]));
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(xv[r], wv[r][e], acc[t][e]);
+    }
+  }
+
+  float mine = 0.f;
+#pragma unroll
+  for (int t = 0; t < kTPB; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[t][e];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      if (lane == t * 8 + e) mine = v;
+    }
+  part[wave][lane] = mine;
+  __syncthreads();
+  if (wave == 0) total[lane] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t >= ntok) return;
+  topk_out(total, t, tok0 + t, E, K, idx, w, logits);
 }
 
 template <bool BF16, bool E8>
@@ -168,6 +284,21 @@ void launch(hipStream_t s, const void *x, const void *wg, int64_t T, int d, int 
                        x, wg, T, d, E, K, idx, w, logits);
 }
 
+template <bool BF16, bool E8>
+void launch_nr(hipStream_t s, const void *h, const void *g, float eps, const void *wg, int64_t T,
+               int d, int E, int K, void *x, int32_t *idx, float *w) {
+  // tokens per workgroup by batch size, as the router alone
+  if (T <= 256)
+    hipLaunchKernelGGL((norm_route_kernel<BF16, E8, 1>), dim3(unsigned(T)), dim3(256), 0, s, h, g,
+                       eps, wg, T, d, E, K, x, idx, w, nullptr);
+  else if (T <= 1024)
+    hipLaunchKernelGGL((norm_route_kernel<BF16, E8, 2>), dim3(unsigned((T + 1) / 2)), dim3(256),
+                       0, s, h, g, eps, wg, T, d, E, K, x, idx, w, nullptr);
+  else
+    hipLaunchKernelGGL((norm_route_kernel<BF16, E8, 4>), dim3(unsigned((T + 3) / 4)), dim3(256),
+                       0, s, h, g, eps, wg, T, d, E, K, x, idx, w, nullptr);
+}
+
 }  // namespace
 
 hipError_t launch_route(bool bf16, const void *x, const void *wg, int64_t T, int d, int E, int K,
@@ -177,6 +308,17 @@ hipError_t launch_route(bool bf16, const void *x, const void *wg, int64_t T, int
   else if (bf16) launch<true, false>(s, x, wg, T, d, E, K, idx, w, logits);
   else if (e8) launch<false, true>(s, x, wg, T, d, E, K, idx, w, logits);
   else launch<false, false>(s, x, wg, T, d, E, K, idx, w, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_route(bool bf16, const void *h, const void *g, float eps, const void *wg,
+                             int64_t T, int d, int E, int K, void *x, int32_t *idx, float *w,
+                             hipStream_t s) {
+  const bool e8 = (E == 8);
+  if (bf16 && e8) launch_nr<true, true>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
+  else if (bf16) launch_nr<true, false>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
+  else if (e8) launch_nr<false, true>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
+  else launch_nr<false, false>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
   return hipGetLastError();
 }
 

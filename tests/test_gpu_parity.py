@@ -573,24 +573,33 @@ def test_block_forward(moe, oracle, name, cfg, path):
         parity.Y_TOL[cfg.dtype] * np.sqrt(np.mean(y_ref ** 2)) + 2.0 ** -23 * np.max(np.abs(h64))
 
 
-def test_block_staged_equals_one_call(moe):
+@pytest.mark.parametrize("T,d,dtype,E", [
+    (250, 256, "bf16", 8), (700, 256, "bf16", 8), (1500, 256, "bf16", 8),
+    (300, 128, "f32", 8), (90, 256, "bf16", 6), (1100, 128, "f32", 4),
+], ids=["bf16_T250", "bf16_T700", "bf16_T1500", "f32_T300", "bf16_E6", "f32_T1100_E4"])
+def test_block_staged_equals_one_call(moe, T, d, dtype, E):
     """moe_rmsnorm + the staged layer + moe_combine_residual reproduce
-    moe_block_forward bit for bit (bf16 output too)."""
-    cfg = mi.Config("bs", T=250, d=256, h=512, wg_std="fan_in_d")
+    moe_block_forward bit for bit (routing, weights and y; bf16 output too).
+    The one call normalises inside the router's kernel; T spans its 1, 2 and 4
+    tokens per workgroup."""
+    std = {} if dtype == "bf16" else dict(w13_std="fan_in_d", w2_std="fan_in_h")
+    cfg = mi.Config("bs", T=T, d=d, h=512, E=E, dtype=dtype, wg_std="fan_in_d", **std)
     inp = mi.make_inputs(cfg, seed=14)
     blk = mi.make_block(cfg, seed=14)
-    for out_dtype in ("f32", "bf16"):
-        y1, _, _, _, dev = _run_block(moe, cfg, inp, blk, "tiled", out_dtype)
-        p = moe.problem(cfg.T, cfg.d, cfg.h, cfg.E, cfg.K, "bf16", out_dtype, "tiled",
-                        moe.FLAG_DOWN_PARTIALS)
-        hdev = parity.device_array(blk["h"], "bf16")
-        x = moe.rmsnorm(p, hdev, parity.device_array(blk["norm_w"], "bf16"), BLOCK_EPS)
+    flags = moe.FLAG_DOWN_PARTIALS if dtype == "bf16" else 0
+    for out_dtype in (("f32", "bf16") if dtype == "bf16" else ("f32",)):
+        y1, idx1, w1, _, dev = _run_block(moe, cfg, inp, blk, "tiled", out_dtype)
+        p = moe.problem(cfg.T, cfg.d, cfg.h, cfg.E, cfg.K, dtype, out_dtype, "tiled", flags)
+        hdev = parity.device_array(blk["h"], dtype)
+        x = moe.rmsnorm(p, hdev, parity.device_array(blk["norm_w"], dtype), BLOCK_EPS)
         idx, w, _ = moe.route(p, x, dev["w_g"])
         offsets, perm, slot, x_perm = moe.permute(p, x, idx)
         act = moe.expert_gate_up(p, x_perm, offsets, dev["w1"], dev["w3"])
         o = moe.expert_down(p, act, offsets, dev["w2"])
         y = moe.combine_residual(p, o, slot, w, hdev)
         torch.cuda.synchronize()
+        assert np.array_equal(parity.host_array(idx), idx1), out_dtype
+        assert np.array_equal(parity.host_array(w).view(np.uint32), w1.view(np.uint32)), out_dtype
         y2 = parity.host_array(y)
         if out_dtype == "bf16":
             y2 = mi.bf16_bits_to_f32(y2)
