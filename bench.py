@@ -140,6 +140,10 @@ def source_hash(files):
     return h.hexdigest()
 
 
+# the dominant kernel is bracketed by HIP events on every GU_EVERY-th timed step
+GU_EVERY = 8
+
+
 def kernel_files(path: str):
     return ["gemm_stream.hip"] if path == "stream" else ["gemm_tiled.hip"]
 
@@ -205,7 +209,10 @@ def main():
     offsets = torch.empty((E + 1,), dtype=torch.int32, device="cuda")
     perm = torch.empty((S,), dtype=torch.int32, device="cuda")
     slot = torch.empty((T, K), dtype=torch.int32, device="cuda")
-    x_perm = torch.empty((S, d), dtype=dt, device="cuda")
+    # bf16: the gate-up kernels read the token rows through perm_token (no x_perm
+    # copy), as moe_forward does; float32 gathers x_perm in the permute
+    rows_direct = cfg.dtype == "bf16"
+    x_perm = None if rows_direct else torch.empty((S, d), dtype=dt, device="cuda")
     act = torch.empty((S, h), dtype=dt, device="cuda")
     o_perm = torch.empty((S, d) if parts == 1 else (parts, S, d), dtype=f32, device="cuda")
     y = torch.empty((T, d), dtype=f32, device="cuda")
@@ -227,12 +234,15 @@ def main():
             if ev is not None:
                 ev[5].record()
         moe.route(p, x_in, dev["w_g"], idx, w)
-        moe.permute(p, x_in, idx, offsets, perm, slot, x_perm)
+        moe.permute(p, x_in, idx, offsets, perm, slot, x_perm, gather=not rows_direct)
         if ev is not None:
             ev[1].record()
         if gu is not None:
             gu[0].record()
-        moe.expert_gate_up(p, x_perm, offsets, ws["w1"], ws["w3"], act)
+        if rows_direct:
+            moe.expert_gate_up_rows(p, x_in, perm, offsets, ws["w1"], ws["w3"], act)
+        else:
+            moe.expert_gate_up(p, x_perm, offsets, ws["w1"], ws["w3"], act)
         if gu is not None:
             gu[1].record()
         if ev is not None:
@@ -255,17 +265,18 @@ def main():
 
     # Timed region: exactly `steps` steps. The only events inside it bracket the
     # dominant kernel (gate-up) on the stream it is launched on (torch's current
-    # stream, which the binding passes to the library).
-    gu_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                 for _ in range(args.steps)]
+    # stream, which the binding passes to the library), on every GU_EVERY-th step
+    # from the first: a pair of events costs about 6 us of a 430 us decode step.
+    gu_steps = list(range(0, args.steps, GU_EVERY))
+    gu_events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in gu_steps}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, gu=gu_events[i])
+        step(i, gu=gu_events.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    gu_ms_live = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in gu_events]))
+    gu_ms_live = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in gu_events.values()]))
     tokens_per_s = T / (ms_step / 1e3)
 
     # Stage breakdown: a separate, shorter pass with events between all stages
@@ -330,7 +341,8 @@ def main():
         roof = {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "algorithmic_bytes": gu_bytes, "avg_launch_ms": round(gu_ms, 5),
-                "traffic": traffic, "traffic_detail": traffic_detail}
+                "launches_timed": len(gu_steps), "traffic": traffic,
+                "traffic_detail": traffic_detail}
         layer = {"hbm_frac": round(layer_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                  "algorithmic_bytes": layer_bytes}
     else:
@@ -338,8 +350,8 @@ def main():
         achieved = gu_flop / (gu_ms / 1e3) / 1e12
         roof = {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "algorithmic_flop": gu_flop,
-                "avg_launch_ms": round(gu_ms, 5), "traffic": traffic,
-                "traffic_detail": traffic_detail}
+                "avg_launch_ms": round(gu_ms, 5), "launches_timed": len(gu_steps),
+                "traffic": traffic, "traffic_detail": traffic_detail}
         layer = {"mfma_frac": round(layer_flop / (ms_step / 1e3) / 1e12 / peak, 4),
                  "algorithmic_flop": layer_flop}
 

@@ -135,7 +135,10 @@ moe_status moe_route(const moe_problem *p, const void *x, const void *w_g,
  *   offsets    [E + 1]  int32 out: segment e is rows offsets[e] .. offsets[e+1]-1
  *   perm_token [S]      int32 out: token of each sorted row (rows >= offsets[E] untouched)
  *   slot_pos   [T, K]   int32 out: sorted row of slot (t, k)
- *   x_perm     [S, d]   dtype out: x_perm[r] = x[perm_token[r]]
+ *   x_perm     [S, d]   dtype out: x_perm[r] = x[perm_token[r]]; or NULL: the
+ *                       index arrays only (x is then not read and may be NULL),
+ *                       for moe_expert_gate_up_rows, which reads the rows
+ *                       through perm_token itself
  */
 moe_status moe_permute(const moe_problem *p, const void *x, const int32_t *topk_idx,
                        int32_t *offsets, int32_t *perm_token, int32_t *slot_pos,
@@ -152,6 +155,22 @@ moe_status moe_permute(const moe_problem *p, const void *x, const int32_t *topk_
  */
 moe_status moe_expert_gate_up(const moe_problem *p, const void *x_perm, const int32_t *offsets,
                               const void *w1, const void *w3, void *act, void *stream);
+
+/*
+ * moe_expert_gate_up with the permute's row gather folded into the
+ * projection's loads: sorted row r is read from x[perm_token[r]] (the
+ * gather/scatter of tokens over experts, ml-canon page, "Questions worth
+ * asking"), so no x_perm copy is made. act is bitwise that of moe_permute's
+ * x_perm through moe_expert_gate_up.
+ *   x          [T, d]   dtype (bf16 only: MOE_ERR_UNSUPPORTED for float32)
+ *   perm_token [S]      int32, as moe_permute writes it; the entries of rows
+ *                       < offsets[E] must lie in [0, T) (not checked on the
+ *                       device: an id out of range reads outside x)
+ *   offsets, w1, w3, act as for moe_expert_gate_up
+ */
+moe_status moe_expert_gate_up_rows(const moe_problem *p, const void *x, const int32_t *perm_token,
+                                   const int32_t *offsets, const void *w1, const void *w3,
+                                   void *act, void *stream);
 
 /*
  * Expert down projection: o_perm[r] = W2_e act[r] for every expert's segment,

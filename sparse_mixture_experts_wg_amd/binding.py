@@ -83,6 +83,7 @@ def _load() -> ctypes.CDLL:
         "moe_route": ([P, vp, vp, vp, vp, vp, vp], i32),
         "moe_permute": ([P, vp, vp, vp, vp, vp, vp, vp], i32),
         "moe_expert_gate_up": ([P, vp, vp, vp, vp, vp, vp], i32),
+        "moe_expert_gate_up_rows": ([P, vp, vp, vp, vp, vp, vp, vp], i32),
         "moe_expert_down": ([P, vp, vp, vp, vp, vp], i32),
         "moe_expert_workspace_bytes": ([P], sz),
         "moe_expert_swiglu": ([P, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
@@ -200,14 +201,19 @@ def route(p: Problem, x, w_g, topk_idx=None, topk_w=None, logits=None, want_logi
 
 
 def permute(p: Problem, x, topk_idx, offsets=None, perm_token=None, slot_pos=None, x_perm=None,
-            stream=None):
+            stream=None, gather: bool = True):
+    """gather=False: the index arrays only (x_perm is returned as None; x may be
+    None), for expert_gate_up_rows."""
     torch = _torch()
     T, d, E, K, S = int(p.T), int(p.d), int(p.E), int(p.K), p.S
     dt = _tdtype(p.dtype)
-    offsets = _empty((E + 1,), torch.int32, x) if offsets is None else offsets
-    perm_token = _empty((S,), torch.int32, x) if perm_token is None else perm_token
-    slot_pos = _empty((T, K), torch.int32, x) if slot_pos is None else slot_pos
-    x_perm = _empty((S, d), dt, x) if x_perm is None else x_perm
+    offsets = _empty((E + 1,), torch.int32, topk_idx) if offsets is None else offsets
+    perm_token = _empty((S,), torch.int32, topk_idx) if perm_token is None else perm_token
+    slot_pos = _empty((T, K), torch.int32, topk_idx) if slot_pos is None else slot_pos
+    if not gather:
+        x_perm = None
+    elif x_perm is None:
+        x_perm = _empty((S, d), dt, x)
     _check(lib.moe_permute(ctypes.byref(p), _ptr(x, "x", (T, d), dt),
                            _ptr(topk_idx, "topk_idx", (T, K), torch.int32),
                            _ptr(offsets, "offsets", (E + 1,), torch.int32),
@@ -226,6 +232,19 @@ def expert_gate_up(p: Problem, x_perm, offsets, w1, w3, act=None, stream=None):
                                   _ptr(offsets, "offsets", (E + 1,), torch.int32),
                                   _ptr(w1, "w1", (E, h, d), dt), _ptr(w3, "w3", (E, h, d), dt),
                                   _ptr(act, "act", (S, h), dt), _stream(stream)))
+    return act
+
+
+def expert_gate_up_rows(p: Problem, x, perm_token, offsets, w1, w3, act=None, stream=None):
+    torch = _torch()
+    T, d, h, E, S = int(p.T), int(p.d), int(p.h), int(p.E), p.S
+    dt = _tdtype(p.dtype)
+    act = _empty((S, h), dt, x) if act is None else act
+    _check(lib.moe_expert_gate_up_rows(ctypes.byref(p), _ptr(x, "x", (T, d), dt),
+                                       _ptr(perm_token, "perm_token", (S,), torch.int32),
+                                       _ptr(offsets, "offsets", (E + 1,), torch.int32),
+                                       _ptr(w1, "w1", (E, h, d), dt), _ptr(w3, "w3", (E, h, d), dt),
+                                       _ptr(act, "act", (S, h), dt), _stream(stream)))
     return act
 
 

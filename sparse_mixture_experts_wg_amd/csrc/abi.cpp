@@ -380,12 +380,12 @@ moe_status moe_permute(const moe_problem *p, const void *x, const int32_t *topk_
                        void *stream) {
   return guarded([&] {
     CHECK(check_problem(p));
-    CHECK(check_ptr(x, "x"));
     CHECK(check_ptr(topk_idx, "topk_idx"));
     CHECK(check_ptr(offsets, "offsets"));
     CHECK(check_ptr(perm_token, "perm_token"));
     CHECK(check_ptr(slot_pos, "slot_pos"));
-    CHECK(check_ptr(x_perm, "x_perm"));
+    CHECK(check_ptr(x_perm, "x_perm", false));
+    if (x_perm) CHECK(check_ptr(x, "x"));  // NULL x_perm: index arrays only
     CHECK(do_permute(p, x, topk_idx, offsets, perm_token, slot_pos, x_perm, as_stream(stream)));
     return ok();
   });
@@ -401,6 +401,25 @@ moe_status moe_expert_gate_up(const moe_problem *p, const void *x_perm, const in
     CHECK(check_ptr(w3, "w3"));
     CHECK(check_ptr(act, "act"));
     CHECK(do_gate_up(p, x_perm, offsets, w1, w3, act, as_stream(stream)));
+    return ok();
+  });
+}
+
+moe_status moe_expert_gate_up_rows(const moe_problem *p, const void *x, const int32_t *perm_token,
+                                   const int32_t *offsets, const void *w1, const void *w3,
+                                   void *act, void *stream) {
+  return guarded([&] {
+    CHECK(check_problem(p));
+    if (p->dtype != MOE_BF16)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "gate-up through perm_token is bf16 only; float32 reads moe_permute's x_perm");
+    CHECK(check_ptr(x, "x"));
+    CHECK(check_ptr(perm_token, "perm_token"));
+    CHECK(check_ptr(offsets, "offsets"));
+    CHECK(check_ptr(w1, "w1"));
+    CHECK(check_ptr(w3, "w3"));
+    CHECK(check_ptr(act, "act"));
+    CHECK(do_gate_up(p, x, offsets, w1, w3, act, as_stream(stream), perm_token));
     return ok();
   });
 }

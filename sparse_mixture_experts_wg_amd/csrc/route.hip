@@ -5,16 +5,18 @@
 // x . W_gate of shape [tokens, 8]; keep the top 2 and renormalise with a
 // softmax) and notion page, sparse-gating equation G(x) = Softmax(TopK(x . W_g)).
 //
-// Layout of the work: a workgroup owns TPB tokens (1, 2 or 4 by batch size: a
-// small batch gets more workgroups, measured faster on MI355X) and its 4
+// Layout of the work: a workgroup owns TPB tokens (1 up to 1024 tokens, else 2:
+// measured fastest on MI355X from T = 1 to 16384) and its 4
 // wavefronts split the dot products into quarters of d, so that even a 1-token
-// batch keeps 4 wavefronts of loads in flight. A lane walks chunks of 8 consecutive rows j:
-// one 16-byte load of x per token (bf16) and the chunk's 8 rows of W_g (8 x 16
-// bytes for bf16 with E = 8; W_g is 64 KiB for d = 4096 and stays in L2),
-// reused by the TPB tokens; two chunks' loads are in flight before their FMAs.
-// Partial sums (TPB tokens x 8 experts in float32) are finished by a butterfly
-// over the 64 lanes and a fixed-order sum of the 4 quarters in LDS. Logits stay
-// float32 up to the top-K decision.
+// batch keeps 4 wavefronts of loads in flight. Within its quarter a wavefront
+// takes 512 rows j at a time, lane L the rows j0 + 64 r + L (r = 0..7): each
+// load instruction of W_g then reads one contiguous kilobyte (64 rows of
+// 8 x bf16) and each load of x 128 contiguous bytes, the fewest cache lines per
+// instruction (8 consecutive rows per lane would touch 64 lines per W_g
+// instruction). W_g (64 KiB for d = 4096) stays in L2 and each row is reused by
+// the TPB tokens. Partial sums (TPB tokens x 8 experts in float32) are finished
+// by a butterfly over the 64 lanes and a fixed-order sum of the 4 quarters in
+// LDS. Logits stay float32 up to the top-K decision.
 #include "kernels.h"
 
 namespace moe {
@@ -41,6 +43,15 @@ __device__ __forceinline__ void load8(const void *base, int64_t elem, float v[8]
       v[4 + i] = b[i];
     }
   }
+}
+
+// One element as float.
+template <bool BF16>
+__device__ __forceinline__ float load1(const void *base, int64_t elem) {
+  if constexpr (BF16)
+    return __uint_as_float(uint32_t(static_cast<const uint16_t *>(base)[elem]) << 16);
+  else
+    return static_cast<const float *>(base)[elem];
 }
 
 // Row j of W_g as 8 floats (experts >= E read as 0).
@@ -120,18 +131,26 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ x,
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
 
-  const int quarter = d >> 5;  // chunks of 8 rows per wavefront (d multiple of 128)
-  const int cbeg = wave * quarter, cend = cbeg + quarter;
-#pragma unroll 2
-  for (int c = cbeg + lane; c < cend; c += 64) {
-    float wv[8][8];  // [row in chunk][expert]
+  // rows [rbeg, rend) of this wavefront (d a multiple of 128); rows past the
+  // end of a 512-row block load row rend - 1 and count as x = 0
+  const int rbeg = wave * (d >> 2), rend = rbeg + (d >> 2);
+  for (int j0 = rbeg; j0 < rend; j0 += 512) {
+    float wv[8][8];  // [r][expert]
+    int jr[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) load_wrow<BF16, E8>(wg, int64_t(c) * 8 + r, E, wv[r]);
+    for (int r = 0; r < 8; ++r) {
+      jr[r] = min(j0 + 64 * r + lane, rend - 1);
+      load_wrow<BF16, E8>(wg, jr[r], E, wv[r]);
+    }
 #pragma unroll
     for (int t = 0; t < kTPB; ++t) {
       if (t >= ntok) continue;
       float xv[8];
-      load8<BF16>(x, (tok0 + t) * d + int64_t(c) * 8, xv);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float v = load1<BF16>(x, (tok0 + t) * d + jr[r]);
+        xv[r] = (j0 + 64 * r + lane < rend) ? v : 0.f;
+      }
 #pragma unroll
       for (int r = 0; r < 8; ++r)
 #pragma unroll
@@ -166,19 +185,6 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ x,
 // wavefront sums added 0+1+2+3), and the logits follow route_kernel's order on
 // the rounded x, so x, the logits and the routing are bitwise those of the two
 // separate kernels.
-template <bool BF16>
-__device__ __forceinline__ void store8(void *base, int64_t elem, const float v[8]) {
-  if constexpr (BF16) {
-    u32x4 q;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = f32_to_bf16_bits(v[2 * i]) | (f32_to_bf16_bits(v[2 * i + 1]) << 16);
-    *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(base) + elem) = q;
-  } else {
-    *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + elem) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + elem + 4) = f32x4{v[4], v[5], v[6], v[7]};
-  }
-}
-
 template <bool BF16, bool E8, int kTPB>
 __global__ __launch_bounds__(256) void norm_route_kernel(
     const void *__restrict__ h, const void *__restrict__ g, float eps,
@@ -222,26 +228,32 @@ __global__ __launch_bounds__(256) void norm_route_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
 
-  const int quarter = d >> 5;
-  const int cbeg = wave * quarter, cend = cbeg + quarter;
-#pragma unroll 2
-  for (int c = cbeg + lane; c < cend; c += 64) {
-    float wv[8][8];
+  const int rbeg = wave * (d >> 2), rend = rbeg + (d >> 2);
+  for (int j0 = rbeg; j0 < rend; j0 += 512) {
+    float wv[8][8], gv[8];
+    int jr[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) load_wrow<BF16, E8>(wg, int64_t(c) * 8 + r, E, wv[r]);
-    float gv[8];
-    load8<BF16>(g, int64_t(c) * 8, gv);
+    for (int r = 0; r < 8; ++r) {
+      jr[r] = min(j0 + 64 * r + lane, rend - 1);
+      load_wrow<BF16, E8>(wg, jr[r], E, wv[r]);
+      gv[r] = load1<BF16>(g, jr[r]);
+    }
 #pragma unroll
     for (int t = 0; t < kTPB; ++t) {
       if (t >= ntok) continue;
       float xv[8];
-      load8<BF16>(h, (tok0 + t) * d + int64_t(c) * 8, xv);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xv[i] = (xv[i] * inv[t]) * gv[i];
-      store8<BF16>(x, (tok0 + t) * d + int64_t(c) * 8, xv);
-      if constexpr (BF16) {  // route on x as stored: rounded once to bf16
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xv[i] = bf16_bits_to_f32(f32_to_bf16_bits(xv[i]));
+      for (int r = 0; r < 8; ++r) {
+        const int64_t el = (tok0 + t) * d + jr[r];
+        float v = (load1<BF16>(h, el) * inv[t]) * gv[r];
+        if constexpr (BF16) {  // x as stored: rounded once to bf16
+          const uint32_t b = f32_to_bf16_bits(v);
+          if (j0 + 64 * r + lane < rend) static_cast<uint16_t *>(x)[el] = uint16_t(b);
+          v = bf16_bits_to_f32(b);
+        } else {
+          if (j0 + 64 * r + lane < rend) static_cast<float *>(x)[el] = v;
+        }
+        xv[r] = (j0 + 64 * r + lane < rend) ? v : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 8; ++r)
@@ -272,30 +284,23 @@ __global__ __launch_bounds__(256) void norm_route_kernel(
 template <bool BF16, bool E8>
 void launch(hipStream_t s, const void *x, const void *wg, int64_t T, int d, int E, int K,
             int32_t *idx, float *w, float *logits) {
-  // tokens per workgroup by batch size (a sweep of T = 1 .. 16384 on MI355X)
-  if (T <= 256)
+  if (T <= 1024)
     hipLaunchKernelGGL((route_kernel<BF16, E8, 1>), dim3(unsigned(T)), dim3(256), 0, s, x, wg, T,
                        d, E, K, idx, w, logits);
-  else if (T <= 1024)
-    hipLaunchKernelGGL((route_kernel<BF16, E8, 2>), dim3(unsigned((T + 1) / 2)), dim3(256), 0, s,
-                       x, wg, T, d, E, K, idx, w, logits);
   else
-    hipLaunchKernelGGL((route_kernel<BF16, E8, 4>), dim3(unsigned((T + 3) / 4)), dim3(256), 0, s,
+    hipLaunchKernelGGL((route_kernel<BF16, E8, 2>), dim3(unsigned((T + 1) / 2)), dim3(256), 0, s,
                        x, wg, T, d, E, K, idx, w, logits);
 }
 
 template <bool BF16, bool E8>
 void launch_nr(hipStream_t s, const void *h, const void *g, float eps, const void *wg, int64_t T,
                int d, int E, int K, void *x, int32_t *idx, float *w) {
-  // tokens per workgroup by batch size, as the router alone
-  if (T <= 256)
+  // tokens per workgroup as the router alone
+  if (T <= 1024)
     hipLaunchKernelGGL((norm_route_kernel<BF16, E8, 1>), dim3(unsigned(T)), dim3(256), 0, s, h, g,
                        eps, wg, T, d, E, K, x, idx, w, nullptr);
-  else if (T <= 1024)
-    hipLaunchKernelGGL((norm_route_kernel<BF16, E8, 2>), dim3(unsigned((T + 1) / 2)), dim3(256),
-                       0, s, h, g, eps, wg, T, d, E, K, x, idx, w, nullptr);
   else
-    hipLaunchKernelGGL((norm_route_kernel<BF16, E8, 4>), dim3(unsigned((T + 3) / 4)), dim3(256),
+    hipLaunchKernelGGL((norm_route_kernel<BF16, E8, 2>), dim3(unsigned((T + 1) / 2)), dim3(256),
                        0, s, h, g, eps, wg, T, d, E, K, x, idx, w, nullptr);
 }
 

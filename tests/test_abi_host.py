@@ -69,6 +69,12 @@ def test_bad_dtype_and_flags():
     p = _p()
     p.path = 5
     assert moe.resolve_path(p) == -binding.ERR_UNSUPPORTED
+    # the gate-up through perm_token is bf16 only (checked before anything is enqueued)
+    p = _p()
+    p.dtype = binding.F32
+    assert lib.moe_expert_gate_up_rows(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       None) == binding.ERR_UNSUPPORTED
+    assert b"bf16 only" in lib.moe_last_error()
 
 
 def test_path_resolution():
@@ -146,6 +152,10 @@ def test_null_and_alignment():
     assert lib.moe_combine(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE + 4, None) == binding.ERR_ALIGN
     assert lib.moe_permute(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == binding.ERR_NULL
     assert lib.moe_expert_gate_up(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, None) == binding.ERR_NULL
+    assert lib.moe_expert_gate_up_rows(ctypes.byref(p), FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                       None) == binding.ERR_NULL
+    # the index-only permute still needs its index arrays
+    assert lib.moe_permute(ctypes.byref(p), None, FAKE, None, FAKE, FAKE, None, None) == binding.ERR_NULL
     assert lib.moe_expert_down(ctypes.byref(p), FAKE, FAKE, None, FAKE, None) == binding.ERR_NULL
 
 

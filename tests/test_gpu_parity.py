@@ -187,10 +187,14 @@ def test_forward_workload(moe, oracle, name):
 
 # ---- single steps ------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", WORKLOADS + ["small_E3"])
+@pytest.mark.parametrize("name", WORKLOADS + ["small_E3", "odd_T1501_d384", "f32_E5_d640"])
 def test_route_step(moe, oracle, name):
     if name == "small_E3":
         cfg = mi.Config("r", T=517, d=256, h=128, E=3, K=2, wg_std="fan_in_d")
+    elif name == "odd_T1501_d384":  # 2 tokens per workgroup, a ragged 512-row block
+        cfg = mi.Config("r", T=1501, d=384, h=128, wg_std="fan_in_d")
+    elif name == "f32_E5_d640":
+        cfg = mi.Config("r", T=2049, d=640, h=128, E=5, K=2, dtype="f32", wg_std="fan_in_d")
     else:
         cfg = mi.CONFIGS[name]
     inp = mi.make_inputs(cfg, seed=0, experts=False)
@@ -411,6 +415,36 @@ def test_expert_steps(moe, oracle, name, path, T, d, h, counts, flags, parts_exp
         parity.check_output(of_h[a:b], ref_f, "bf16", f"swiglu expert {e}")
 
 
+@pytest.mark.parametrize("path,T,d,h,cap", [
+    ("stream", 1, 256, 384, 0), ("stream", 40, 256, 384, 0), ("stream", 112, 384, 256, 9),
+    ("tiled", 100, 256, 512, 0), ("tiled", 350, 256, 512, 0), ("tiled", 1200, 384, 256, 0),
+    ("tiled", 600, 256, 256, 100),
+], ids=["stream_T1", "stream_T40", "stream_T112_cap9", "tiled64_T100", "tiled128_T350",
+        "tiled256_T1200", "tiled_cap100"])
+def test_gate_up_rows_equals_gathered(moe, path, T, d, h, cap):
+    """moe_expert_gate_up_rows (rows read through perm_token) gives bitwise the
+    act of moe_permute's x_perm through moe_expert_gate_up; the index-only
+    permute writes the same index arrays as the gathering one."""
+    cfg = mi.Config("gr", T=T, d=d, h=h, wg_std="fan_in_d")
+    inp = mi.make_inputs(cfg, seed=21)
+    dev = parity.upload_inputs(inp, "bf16")
+    p = moe.problem(T, d, h, 8, 2, "bf16", "f32", path, capacity=cap)
+    _say(f"gate_up_rows {path} T={T} d={d} h={h} cap={cap}")
+    idx, _, _ = moe.route(p, dev["x"], dev["w_g"])
+    off, perm, slot, xp = moe.permute(p, dev["x"], idx)
+    off2, perm2, slot2, none = moe.permute(p, None, idx, gather=False)
+    assert none is None
+    act = moe.expert_gate_up(p, xp, off, dev["w1"], dev["w3"])
+    act2 = moe.expert_gate_up_rows(p, dev["x"], perm2, off2, dev["w1"], dev["w3"])
+    torch.cuda.synchronize()
+    o = parity.host_array(off)
+    assert np.array_equal(o, parity.host_array(off2))
+    n = int(o[-1])
+    assert np.array_equal(parity.host_array(perm)[:n], parity.host_array(perm2)[:n])
+    assert np.array_equal(parity.host_array(slot), parity.host_array(slot2))
+    assert np.array_equal(parity.host_array(act)[:n], parity.host_array(act2)[:n])
+
+
 def test_combine_step(moe):
     T, K, d = 257, 2, 384
     rng = np.random.default_rng(9)
@@ -574,14 +608,14 @@ def test_block_forward(moe, oracle, name, cfg, path):
 
 
 @pytest.mark.parametrize("T,d,dtype,E", [
-    (250, 256, "bf16", 8), (700, 256, "bf16", 8), (1500, 256, "bf16", 8),
+    (250, 256, "bf16", 8), (700, 256, "bf16", 8), (1501, 256, "bf16", 8),
     (300, 128, "f32", 8), (90, 256, "bf16", 6), (1100, 128, "f32", 4),
-], ids=["bf16_T250", "bf16_T700", "bf16_T1500", "f32_T300", "bf16_E6", "f32_T1100_E4"])
+], ids=["bf16_T250", "bf16_T700", "bf16_T1501", "f32_T300", "bf16_E6", "f32_T1100_E4"])
 def test_block_staged_equals_one_call(moe, T, d, dtype, E):
     """moe_rmsnorm + the staged layer + moe_combine_residual reproduce
     moe_block_forward bit for bit (routing, weights and y; bf16 output too).
-    The one call normalises inside the router's kernel; T spans its 1, 2 and 4
-    tokens per workgroup."""
+    The one call normalises inside the router's kernel; T spans its 1 and 2
+    tokens per workgroup and an odd count in the last workgroup."""
     std = {} if dtype == "bf16" else dict(w13_std="fan_in_d", w2_std="fan_in_h")
     cfg = mi.Config("bs", T=T, d=d, h=512, E=E, dtype=dtype, wg_std="fan_in_d", **std)
     inp = mi.make_inputs(cfg, seed=14)
