@@ -26,7 +26,9 @@
  *    with a message from moe_last_error() (per thread). A device fault surfaces
  *    at the caller's next synchronisation.
  *  - Supported problems: 1 <= E <= 8, K in {1, 2}, K <= E, T >= 1,
- *    T <= 2^26, d and h positive multiples of 128 up to 2^20, h*d < 2^31.
+ *    T <= 2^26 and T * ceil(d / 1024) < 2^24, d and h positive multiples of
+ *    128 up to 2^20, h*d < 2^31; the tiled path also bounds its grid (column
+ *    blocks x token blocks), MOE_ERR_UNSUPPORTED past it.
  *  - Results are deterministic: no atomics take part in any value, and every
  *    sum has a fixed order.
  */

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -35,6 +36,9 @@ size_t esize(int dt) { return dt == MOE_BF16 ? 2 : 4; }
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 int resolve(const moe_problem *p);
+
+int gate_up_tile(const moe_problem *p);
+int down_tile(const moe_problem *p);
 
 moe_status check_problem(const moe_problem *p) {
   if (!p) return fail(MOE_ERR_NULL, "problem descriptor is NULL");
@@ -68,15 +72,21 @@ moe_status check_problem(const moe_problem *p) {
   if (p->reserved != 0) return fail(MOE_ERR_UNSUPPORTED, "reserved field must be 0");
   if (p->flags & ~MOE_FLAG_DOWN_PARTIALS)
     return fail(MOE_ERR_UNSUPPORTED, "flags=0x%x: unknown bits", unsigned(p->flags));
-  // tiled grids: column blocks x (token blocks + E) (x 4 partial sums for the
-  // down projection) must fit a 1-D grid and 32-bit tile arithmetic; a batch
-  // with more than 96 rows per expert uses 256-token blocks, a smaller one has
-  // few blocks anyway
+  // HIP counts the work-items of a grid dimension in 32 bits. The largest 1-D
+  // grids are the combine's (T * ceil(d / 1024) workgroups of 256; the router,
+  // the norm and the gather launch fewer) and the tiled GEMMs' (column blocks x
+  // (token blocks + E), x at most 4 partial sums for the down projection,
+  // workgroups of 512).
+  const int64_t kMaxItems = (int64_t(1) << 32) - 1;
   const int64_t S = p->T * p->K;
-  const int64_t tiles_gu = (p->h / 128) * ((S + 255) / 256 + p->E);
-  const int64_t tiles_dn = 4 * ((p->d + 255) / 256) * ((S + 255) / 256 + p->E);
-  if (tiles_gu > kMaxIndex / 2 || tiles_dn > kMaxIndex / 2)
-    return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (p->T * ((p->d + 1023) / 1024) * 256 > kMaxItems)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "T=%lld d=%lld: T * ceil(d / 1024) must stay below 2^24 (grid size)",
+                (long long)p->T, (long long)p->d);
+  const int64_t tiles_gu = (p->h / 128) * ((S + gate_up_tile(p) - 1) / gate_up_tile(p) + p->E);
+  const int64_t tiles_dn = 4 * ((p->d + 255) / 256) * ((S + down_tile(p) - 1) / down_tile(p) + p->E);
+  if ((std::max(tiles_gu, tiles_dn) + 7) / 8 * 8 * 512 > kMaxItems)
+    return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch (tiled grid size)");
   // stream grid: S / 32 row groups in the z dimension
   if (p->dtype == MOE_BF16 && resolve(p) == MOE_PATH_STREAM && (S + 31) / 32 >= (int64_t(1) << 16))
     return fail(MOE_ERR_UNSUPPORTED, "T=%lld too large for the STREAM path (use TILED)",

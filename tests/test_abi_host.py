@@ -46,6 +46,11 @@ def test_status_strings():
     (dict(T=1 << 31), binding.ERR_UNSUPPORTED),
     # the streaming path takes at most 2^21 routed rows (row groups in the grid's z)
     (dict(T=1 << 20, path="stream"), binding.ERR_UNSUPPORTED),
+    # 32-bit work-item counts of the combine grid: T * ceil(d / 1024) < 2^24
+    (dict(T=1 << 24, d=128), binding.ERR_UNSUPPORTED),
+    (dict(T=1 << 22, d=4096), binding.ERR_UNSUPPORTED),
+    # the tiled grid: h / 128 column blocks x token blocks of 256
+    (dict(T=1 << 23, d=128, h=1 << 17), binding.ERR_UNSUPPORTED),
 ])
 def test_problem_validation(kw, code):
     p = _p(**kw)
@@ -54,6 +59,13 @@ def test_problem_validation(kw, code):
     st = lib.moe_route(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None)
     assert st == code, moe.last_error()
     assert moe.last_error()
+
+
+def test_grid_limits_accept_the_largest_fitting_batch():
+    # the largest T whose combine grid fits: 2^24 - 1 workgroups of 256
+    assert moe.resolve_path(_p(T=(1 << 24) - 1, d=128, h=128)) == binding.PATH_TILED
+    assert moe.resolve_path(_p(T=(1 << 22) - 1, d=4096, h=128)) == binding.PATH_TILED
+    assert moe.resolve_path(_p(T=1 << 20, d=4096, h=14336)) == binding.PATH_TILED
 
 
 def test_bad_dtype_and_flags():
