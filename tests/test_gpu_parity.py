@@ -53,6 +53,25 @@ def _run_forward(moe, cfg, inp, path="auto", out_dtype="f32"):
     return yh.astype(np.float64), parity.host_array(idx), parity.host_array(w), dev, p
 
 
+def _run_staged_as_bench(moe, cfg, dev):
+    """The staged entry points in bench.py's launch configuration: partial sums
+    allowed in the down projection and, for bf16, the token rows read through
+    perm_token instead of a gathered copy."""
+    p = moe.problem(cfg.T, cfg.d, cfg.h, cfg.E, cfg.K, cfg.dtype, "f32", "auto",
+                    moe.FLAG_DOWN_PARTIALS)
+    idx, w, _ = moe.route(p, dev["x"], dev["w_g"])
+    if cfg.dtype == "bf16":
+        off, perm, slot, _ = moe.permute(p, dev["x"], idx, gather=False)
+        act = moe.expert_gate_up_rows(p, dev["x"], perm, off, dev["w1"], dev["w3"])
+    else:
+        off, perm, slot, xp = moe.permute(p, dev["x"], idx)
+        act = moe.expert_gate_up(p, xp, off, dev["w1"], dev["w3"])
+    o = moe.expert_down(p, act, off, dev["w2"])
+    y = moe.combine(p, o, slot, w)
+    torch.cuda.synchronize()
+    return parity.host_array(y).astype(np.float64)
+
+
 # ---- whole layer, small shapes (every token compared) ------------------------------
 
 SMALL = [
@@ -172,7 +191,10 @@ def test_forward_workload(moe, oracle, name):
     inp = mi.make_inputs(cfg, seed=0)
     _say("  running GPU forward")
     y, idx, w, dev, p = _run_forward(moe, cfg, inp, "auto")
+    _say("  running the staged steps as bench.py times them")
+    y_st = _run_staged_as_bench(moe, cfg, dev)
     del dev
+    assert np.array_equal(y_st, y), "staged steps differ from moe_forward"
     toks = parity.sample_tokens(cfg.T, SAMPLE if cfg.T > 64 else cfg.T, seed=0)
     _say(f"  oracle on {len(toks)} tokens")
     toks, y_ref, diff, margin = _layer_ref(oracle, inp, cfg, toks, idx, w)
