@@ -62,7 +62,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 } moe_path;
 
 /* Largest T for which MOE_PATH_AUTO picks MOE_PATH_STREAM. */
-#define MOE_STREAM_MAX_T 112
+#define MOE_STREAM_MAX_T 72
 
 /* moe_problem.capacity (the capacity variant; the pages name the capacity
  * factor, a cap on the tokens per expert, as general MoE practice: ml-canon

@@ -91,8 +91,8 @@ def test_bad_dtype_and_flags():
 
 def test_path_resolution():
     # the automatic switch point comes from a batch-size sweep on MI355X (bench.py --sweep)
-    assert moe.resolve_path(_p(T=112)) == binding.PATH_STREAM
-    assert moe.resolve_path(_p(T=113)) == binding.PATH_TILED
+    assert moe.resolve_path(_p(T=72)) == binding.PATH_STREAM
+    assert moe.resolve_path(_p(T=73)) == binding.PATH_TILED
     assert moe.resolve_path(_p(T=4096, path="stream")) == binding.PATH_STREAM
     assert moe.resolve_path(_p(T=8, path="tiled")) == binding.PATH_TILED
     assert moe.resolve_path(_p(dtype="f32")) == binding.PATH_TILED

@@ -81,8 +81,8 @@ SMALL = [
     # about 1024 rows per expert, every token compared
     ("bf16_tiled_T4096", mi.Config("s1b", T=4096, d=256, h=512, wg_std="fan_in_d"), "auto"),
     ("bf16_tiled_T65", mi.Config("s2", T=65, d=384, h=256, wg_std="fan_in_d"), "tiled"),
-    ("bf16_auto_T113_tiled", mi.Config("s2b", T=113, d=384, h=256, wg_std="fan_in_d"), "auto"),
-    ("bf16_auto_T112_stream", mi.Config("s2c", T=112, d=256, h=384, wg_std="fan_in_d"), "auto"),
+    ("bf16_auto_T73_tiled", mi.Config("s2b", T=73, d=384, h=256, wg_std="fan_in_d"), "auto"),
+    ("bf16_auto_T72_stream", mi.Config("s2c", T=72, d=256, h=384, wg_std="fan_in_d"), "auto"),
     ("bf16_tiled_T193", mi.Config("s2d", T=193, d=384, h=256, wg_std="fan_in_d"), "tiled"),
     ("bf16_stream_T64", mi.Config("s3", T=64, d=512, h=1024, wg_std="fan_in_d"), "auto"),
     ("bf16_stream_T7", mi.Config("s4", T=7, d=256, h=384, wg_std="fan_in_d"), "stream"),
