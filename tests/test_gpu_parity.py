@@ -84,6 +84,8 @@ SMALL = [
     ("bf16_auto_T73_tiled", mi.Config("s2b", T=73, d=384, h=256, wg_std="fan_in_d"), "auto"),
     ("bf16_auto_T72_stream", mi.Config("s2c", T=72, d=256, h=384, wg_std="fan_in_d"), "auto"),
     ("bf16_tiled_T193", mi.Config("s2d", T=193, d=384, h=256, wg_std="fan_in_d"), "tiled"),
+    # about 113 rows per expert: still 128-token tiles (n + sqrt(n) <= 128)
+    ("bf16_tiled128_T450", mi.Config("s2e", T=450, d=256, h=512, wg_std="fan_in_d"), "auto"),
     ("bf16_stream_T64", mi.Config("s3", T=64, d=512, h=1024, wg_std="fan_in_d"), "auto"),
     ("bf16_stream_T7", mi.Config("s4", T=7, d=256, h=384, wg_std="fan_in_d"), "stream"),
     ("bf16_stream_T100_multigroup", mi.Config("s5", T=100, d=256, h=256, wg_std="fan_in_d"),
