@@ -218,6 +218,10 @@ __global__ __launch_bounds__(256) void norm_route_kernel(
   float inv[kTPB];
 #pragma unroll
   for (int t = 0; t < kTPB; ++t) {
+    if (t >= ntok) {  // no token: its sums were never written
+      inv[t] = 0.f;
+      continue;
+    }
     const float ms = (((ssp[t][0] + ssp[t][1]) + ssp[t][2]) + ssp[t][3]) / float(d);
     inv[t] = 1.0f / sqrtf(ms + eps);
   }
