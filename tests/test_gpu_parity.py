@@ -243,6 +243,15 @@ PERMUTE_CASES = [
     ("one_expert", 100, 1, 1),
     ("k1", 777, 8, 1),
     ("big", 40000, 8, 2),
+    # the index kernel stages slots in LDS from 2048 up to 32768 slots, and the
+    # row -> token map as well up to 16384: both sides of each boundary
+    ("slots_2047", 2047, 8, 1),
+    ("slots_2048", 1024, 8, 2),
+    ("slots_16384", 8192, 8, 2),
+    ("slots_16385", 16385, 5, 1),
+    ("slots_20000", 10000, 8, 2),
+    ("slots_32768", 16384, 8, 2),
+    ("slots_32769", 32769, 3, 1),
 ]
 
 
@@ -289,7 +298,9 @@ def test_permute_all_to_one_and_dropped_ids(moe, oracle):
 # ---- capacity variant ---------------------------------------------------------------
 
 @pytest.mark.parametrize("T,E,K,cap", [(700, 8, 2, 1), (700, 8, 2, 50), (700, 8, 2, 175),
-                                       (700, 8, 2, 100000), (333, 3, 1, 40), (64, 8, 2, 3)])
+                                       (700, 8, 2, 100000), (333, 3, 1, 40), (64, 8, 2, 3),
+                                       (5000, 8, 2, 1200), (10000, 8, 2, 2400),
+                                       (20000, 8, 2, 4900)])
 def test_permute_capacity_exact(moe, oracle, T, E, K, cap):
     idx = mi.make_routing(T, E, K, seed=T + cap)
     idx[: T // 2, 0] = 0  # crowd expert 0 so that the cap bites
