@@ -94,6 +94,12 @@ SMALL = [
     ("bf16_E4_K1", mi.Config("s7", T=300, d=256, h=384, E=4, K=1, wg_std="fan_in_d"), "auto"),
     ("bf16_E3_K2_stream", mi.Config("s8", T=40, d=128, h=256, E=3, K=2, wg_std="fan_in_d"),
      "stream"),
+    # one expert: the layer is a dense SwiGLU FFN (w = 1); two experts with K = 2: a full
+    # softmax over both
+    ("bf16_E1_K1_tiled", mi.Config("s10", T=500, d=256, h=384, E=1, K=1, wg_std="fan_in_d"),
+     "auto"),
+    ("bf16_E2_K2_stream", mi.Config("s11", T=20, d=256, h=256, E=2, K=2, wg_std="fan_in_d"),
+     "auto"),
     ("f32_ragged", mi.Config("s9", T=333, d=128, h=384, dtype="f32", w13_std="fan_in_d",
                              w2_std="fan_in_h"), "auto"),
 ]
