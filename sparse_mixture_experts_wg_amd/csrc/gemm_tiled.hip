@@ -29,8 +29,8 @@
 //    fastest, so concurrently running tiles share weight tiles; the linear tile
 //    id is remapped so that each of the 8 XCDs (workgroups are dealt to XCDs
 //    round-robin) owns one contiguous range of tiles and its own L2 sees the
-//    reuse. Token rows past an expert's end are clamped duplicates whose results
-//    are never stored.
+//    reuse. Token rows past an expert's end read a row of zeros (g_zero_row);
+//    their results are never stored.
 //  * Down can split the sum over h into `ksplit` parts: each part is a tile of
 //    its own writing float32 partial sums that the combine step adds in a fixed
 //    order, so that the last round of tiles fills the GPU.
@@ -44,6 +44,15 @@ namespace {
 
 constexpr int kXCD = 8;
 typedef __attribute__((address_space(3))) void lds_void;
+
+// A row of zeros in device memory (static storage, zeroed when the code object
+// loads). The rows of a token tile past its expert's end copy from it instead
+// of duplicating a real row: their results are never stored, and matrix
+// instructions on zero operands draw less power, which the power-limited clock
+// returns as speed (0.2-3% per launch, most where tiles are mostly padding).
+// Longer rows (K > kZeroK) fall back to the duplicates.
+constexpr int kZeroK = 65536;
+__device__ __attribute__((aligned(1024))) uint16_t g_zero_row[kZeroK];
 
 // s_waitcnt immediates: vmcnt(0) / vmcnt(4) with the other counters at their maximum.
 constexpr int kWaitVm0 = 0x0F70;
@@ -203,8 +212,12 @@ __global__ __launch_bounds__(512) void tiled256_kernel(const uint16_t *__restric
     if constexpr (GATEUP) wrow = tl.c0 + ((r >> 7) << 6) + (r & 63);
     else wrow = min(tl.c0 + r, N - 1);
     wofs[i] = uint32_t(wrow) * uint32_t(K) + c * 8;
-    const int xr = tl.row0 + tl.m0 + min(r, tl.ne - 1 - tl.m0);
-    xsrc[i] = X + size_t(rowmap ? rowmap[xr] : xr) * K + c * 8;
+    if (r > tl.ne - 1 - tl.m0 && K <= kZeroK) {
+      xsrc[i] = g_zero_row + c * 8;
+    } else {
+      const int xr = tl.row0 + tl.m0 + min(r, tl.ne - 1 - tl.m0);
+      xsrc[i] = X + size_t(rowmap ? rowmap[xr] : xr) * K + c * 8;
+    }
   }
   const int dma_row = wave * 32;
 
@@ -367,8 +380,13 @@ __device__ __forceinline__ void small_body(
   for (int i = 0; i < XI; ++i) {
     const int lr = lane >> 3;
     const int q = (dma_xrow / 8 + i) & 3;
-    const int xr = row0 + m0 + min(dma_xrow + 8 * i + lr, xlim);
-    xsrc[i] = X + size_t(rowmap ? rowmap[xr] : xr) * K + (((lane & 7) ^ lr ^ q) << 3);
+    const int chunk = ((lane & 7) ^ lr ^ q) << 3;
+    if (dma_xrow + 8 * i + lr > xlim && K <= kZeroK) {
+      xsrc[i] = g_zero_row + chunk;  // padding row
+    } else {
+      const int xr = row0 + m0 + min(dma_xrow + 8 * i + lr, xlim);
+      xsrc[i] = X + size_t(rowmap ? rowmap[xr] : xr) * K + chunk;
+    }
   }
 
   // ---- fragment read addresses (bytes): row (lane & 31) of a 32-row group,
