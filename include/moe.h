@@ -57,12 +57,17 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Expert-projection variant. STREAM: weight streaming for small batches (an
  * expert's rows are taken 32 or 64 at a time, each group streaming the expert's
  * weights; at most 2^21 routed rows); TILED: LDS-tiled matrix-core GEMM for
- * large batches. AUTO picks STREAM when T <= MOE_STREAM_MAX_T, else TILED.
+ * large batches. AUTO picks STREAM when T <= MOE_STREAM_MAX_T (d <= 4096) or
+ * T <= MOE_STREAM_MAX_T_WIDE (larger d), else TILED.
  * float32 problems always use one plain tiled kernel. */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 } moe_path;
 
-/* Largest T for which MOE_PATH_AUTO picks MOE_PATH_STREAM. */
+/* Largest T for which MOE_PATH_AUTO picks MOE_PATH_STREAM: MOE_STREAM_MAX_T
+ * for d <= 4096, MOE_STREAM_MAX_T_WIDE for larger d (batch-size sweeps on
+ * MI355X at the Mixtral 8x7B shape, d = 4096, h = 14336, and the 8x22B shape,
+ * d = 6144, h = 16384). */
 #define MOE_STREAM_MAX_T 72
+#define MOE_STREAM_MAX_T_WIDE 32
 
 /* moe_problem.capacity (the capacity variant; the pages name the capacity
  * factor, a cap on the tokens per expert, as general MoE practice: ml-canon

@@ -97,7 +97,8 @@ moe_status check_problem(const moe_problem *p) {
 int resolve(const moe_problem *p) {
   if (p->dtype == MOE_F32) return MOE_PATH_TILED;
   if (p->path != MOE_PATH_AUTO) return p->path;
-  return p->T <= MOE_STREAM_MAX_T ? MOE_PATH_STREAM : MOE_PATH_TILED;
+  const int64_t max_t = p->d <= 4096 ? MOE_STREAM_MAX_T : MOE_STREAM_MAX_T_WIDE;
+  return p->T <= max_t ? MOE_PATH_STREAM : MOE_PATH_TILED;
 }
 
 moe_status check_ptr(const void *ptr, const char *name, bool required = true) {

@@ -93,6 +93,10 @@ def test_path_resolution():
     # the automatic switch point comes from a batch-size sweep on MI355X (bench.py --sweep)
     assert moe.resolve_path(_p(T=72)) == binding.PATH_STREAM
     assert moe.resolve_path(_p(T=73)) == binding.PATH_TILED
+    assert moe.resolve_path(_p(T=72, d=4096)) == binding.PATH_STREAM
+    # wider models switch earlier (the 8x22B shape, d = 6144)
+    assert moe.resolve_path(_p(T=32, d=6144, h=16384)) == binding.PATH_STREAM
+    assert moe.resolve_path(_p(T=33, d=6144, h=16384)) == binding.PATH_TILED
     assert moe.resolve_path(_p(T=4096, path="stream")) == binding.PATH_STREAM
     assert moe.resolve_path(_p(T=8, path="tiled")) == binding.PATH_TILED
     assert moe.resolve_path(_p(dtype="f32")) == binding.PATH_TILED
