@@ -21,6 +21,11 @@
 // is C or more is dropped (slot_pos -1, no row) and the offsets count the kept
 // rows min(n_e, C) only.
 //
+// permute_index_small: up to 64 slots (a decode batch) one wavefront does the
+// same sort: lane s holds slot s, a ballot per expert gives the expert's count
+// and the slot's rank among the lanes below it, so no barrier and no LDS are
+// needed; the results are those of permute_index.
+//
 // gather_rows: one wavefront per sorted row copies x[perm_token[r]] with 16-byte
 // loads/stores.
 #include "kernels.h"
@@ -149,6 +154,33 @@ __global__ __launch_bounds__(kThreads) void permute_index_kernel(
   }
 }
 
+constexpr int kSmallSlots = 64;
+
+__global__ __launch_bounds__(64) void permute_index_small_kernel(
+    const int32_t *__restrict__ idx, int S, int K, int E, int capacity,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm_token,
+    int32_t *__restrict__ slot_pos) {
+  const int lane = threadIdx.x;
+  const int e = lane < S ? idx[lane] : -1;
+  const int cap = capacity > 0 ? capacity : 0x7FFFFFFF;
+  const uint64_t below = (uint64_t(1) << lane) - 1;  // lanes 0 .. lane-1
+  int run = 0, my_off = 0, my_rank = 0;
+  for (int q = 0; q < E; ++q) {  // E <= 8, the same in every lane
+    const uint64_t m = __ballot(e == q);
+    if (lane == q) offsets[q] = run;
+    if (e == q) {
+      my_off = run;
+      my_rank = __popcll(m & below);
+    }
+    run += min(int(__popcll(m)), cap);
+  }
+  if (lane == 0) offsets[E] = run;
+  if (lane >= S) return;
+  const int p = (e >= 0 && e < E && my_rank < cap) ? my_off + my_rank : -1;
+  slot_pos[lane] = p;
+  if (p >= 0) perm_token[p] = lane / K;
+}
+
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restrict__ x,
                                                           const int32_t *__restrict__ perm_token,
                                                           const int32_t *__restrict__ offsets,
@@ -168,8 +200,12 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restric
 hipError_t launch_permute_index(const int32_t *idx, int64_t S, int K, int E, int capacity,
                                 int32_t *offsets, int32_t *perm_token, int32_t *slot_pos,
                                 hipStream_t s) {
-  hipLaunchKernelGGL(permute_index_kernel, dim3(1), dim3(kThreads), 0, s, idx, S, K, E, capacity,
-                     offsets, perm_token, slot_pos);
+  if (S <= kSmallSlots)
+    hipLaunchKernelGGL(permute_index_small_kernel, dim3(1), dim3(64), 0, s, idx, int(S), K, E,
+                       capacity, offsets, perm_token, slot_pos);
+  else
+    hipLaunchKernelGGL(permute_index_kernel, dim3(1), dim3(kThreads), 0, s, idx, S, K, E,
+                       capacity, offsets, perm_token, slot_pos);
   return hipGetLastError();
 }
 

@@ -251,6 +251,11 @@ PERMUTE_CASES = [
     ("big", 40000, 8, 2),
     # the index kernel stages slots in LDS from 2048 up to 32768 slots, and the
     # row -> token map as well up to 16384: both sides of each boundary
+    # up to 64 slots one wavefront sorts them (a decode batch: T = 32, K = 2)
+    ("slots_64", 32, 8, 2),
+    ("slots_63", 63, 8, 1),
+    ("slots_65", 65, 8, 1),
+    ("slots_42_E3", 21, 3, 2),
     ("slots_2047", 2047, 8, 1),
     ("slots_2048", 1024, 8, 2),
     ("slots_16384", 8192, 8, 2),
@@ -277,8 +282,9 @@ def test_permute_step_exact(moe, oracle, case, T, E, K):
     assert np.array_equal(parity.host_array(xp), x[perm_r])
 
 
-def test_permute_all_to_one_and_dropped_ids(moe, oracle):
-    T, E, K, d = 300, 8, 2, 256
+@pytest.mark.parametrize("T", [300, 32], ids=["T300", "T32_one_wavefront"])
+def test_permute_all_to_one_and_dropped_ids(moe, oracle, T):
+    E, K, d = 8, 2, 256
     idx = np.zeros((T, K), dtype=np.int32)
     idx[:, 1] = 3
     idx[7, 0] = -1   # dropped
@@ -305,6 +311,7 @@ def test_permute_all_to_one_and_dropped_ids(moe, oracle):
 
 @pytest.mark.parametrize("T,E,K,cap", [(700, 8, 2, 1), (700, 8, 2, 50), (700, 8, 2, 175),
                                        (700, 8, 2, 100000), (333, 3, 1, 40), (64, 8, 2, 3),
+                                       (32, 8, 2, 3), (40, 5, 1, 2),
                                        (5000, 8, 2, 1200), (10000, 8, 2, 2400),
                                        (20000, 8, 2, 4900)])
 def test_permute_capacity_exact(moe, oracle, T, E, K, cap):
