@@ -215,6 +215,27 @@ def test_forward_workload(moe, oracle, name):
         assert abs(share[0] - mi.zipf_shares()[0]) < 5e-3
 
 
+def test_forward_large_batch(moe, oracle):
+    """2^18 tokens (524,288 slots: the permute far past its LDS staging, a tiled
+    grid of about 2^16 workgroups): the permutation exactly, the routing of every
+    token and the output of sampled tokens against the oracle."""
+    cfg = mi.Config("big", T=1 << 18, d=128, h=256, wg_std="fan_in_d")
+    _say(f"large batch: T={cfg.T} d={cfg.d} h={cfg.h}")
+    inp = mi.make_inputs(cfg, seed=5)
+    y, idx, w, dev, p = _run_forward(moe, cfg, inp, "auto")
+    off, perm, slot, none = moe.permute(p, None, parity.device_array(idx, "i32"), gather=False)
+    torch.cuda.synchronize()
+    assert none is None
+    off_r, perm_r, slot_r = oracle.permute(idx, cfg.E)
+    assert np.array_equal(parity.host_array(off), off_r)
+    assert np.array_equal(parity.host_array(perm), perm_r)
+    assert np.array_equal(parity.host_array(slot), slot_r)
+    toks = parity.sample_tokens(cfg.T, 64, seed=1)
+    toks, y_ref, diff, _ = _layer_ref(oracle, inp, cfg, toks, idx, w)
+    rel = parity.check_output(y[toks], y_ref, cfg.dtype, "large batch")
+    _say(f"  max|err|/RMS = {rel:.3e} on {len(toks)} tokens, near-tie set changes: {len(diff)}")
+
+
 # ---- single steps ------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", WORKLOADS + ["small_E3", "odd_T1501_d384", "f32_E5_d640"])
