@@ -102,6 +102,10 @@ SMALL = [
      "auto"),
     ("f32_ragged", mi.Config("s9", T=333, d=128, h=384, dtype="f32", w13_std="fan_in_d",
                              w2_std="fan_in_h"), "auto"),
+    # extreme widths: h above the 65536-element zero row (the down projection's padding
+    # rows fall back to duplicates), and a wide d for the router and the gate-up
+    ("bf16_wide_h", mi.Config("s12", T=300, d=128, h=65664, wg_std="fan_in_d"), "auto"),
+    ("bf16_wide_d", mi.Config("s13", T=200, d=16384, h=128, wg_std="fan_in_d"), "auto"),
 ]
 
 
