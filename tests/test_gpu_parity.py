@@ -106,6 +106,12 @@ SMALL = [
     # rows fall back to duplicates), and a wide d for the router and the gate-up
     ("bf16_wide_h", mi.Config("s12", T=300, d=128, h=65664, wg_std="fan_in_d"), "auto"),
     ("bf16_wide_d", mi.Config("s13", T=200, d=16384, h=128, wg_std="fan_in_d"), "auto"),
+    # the same widths on the streaming path (h = 128: two k-stages over four wavefronts,
+    # so two of them have none)
+    ("bf16_stream_wide_h", mi.Config("s14", T=20, d=128, h=65664, wg_std="fan_in_d"),
+     "stream"),
+    ("bf16_stream_wide_d", mi.Config("s15", T=20, d=16384, h=128, wg_std="fan_in_d"),
+     "stream"),
 ]
 
 
