@@ -199,6 +199,25 @@ __global__ __launch_bounds__(256) void norm_route_kernel(
   const int ntok = int(min(int64_t(kTPB), T - tok0));
   const int chunks = d >> 3;
 
+  // The first 512-row block's weights, gains and inputs do not depend on the
+  // norm: their loads go out before the mean square is formed, so that the two
+  // passes over h do not wait for memory one after the other.
+  const int rbeg = wave * (d >> 2), rend = rbeg + (d >> 2);
+  float wv[8][8], gv[8], hv[kTPB][8];
+  int jr[8];
+#define NR_LOAD_BLOCK(J0)                                                                  \
+  {                                                                                        \
+    _Pragma("unroll") for (int r = 0; r < 8; ++r) {                                        \
+      jr[r] = min((J0) + 64 * r + lane, rend - 1);                                         \
+      load_wrow<BF16, E8>(wg, jr[r], E, wv[r]);                                            \
+      gv[r] = load1<BF16>(g, jr[r]);                                                       \
+    }                                                                                      \
+    _Pragma("unroll") for (int t = 0; t < kTPB; ++t)                                       \
+      _Pragma("unroll") for (int r = 0; r < 8; ++r)                                        \
+        hv[t][r] = load1<BF16>(h, (tok0 + min(t, ntok - 1)) * d + jr[r]);                  \
+  }
+  NR_LOAD_BLOCK(rbeg)
+
   // mean square per token, in norm.hip's order
 #pragma unroll
   for (int t = 0; t < kTPB; ++t) {
@@ -232,16 +251,8 @@ __global__ __launch_bounds__(256) void norm_route_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
 
-  const int rbeg = wave * (d >> 2), rend = rbeg + (d >> 2);
   for (int j0 = rbeg; j0 < rend; j0 += 512) {
-    float wv[8][8], gv[8];
-    int jr[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      jr[r] = min(j0 + 64 * r + lane, rend - 1);
-      load_wrow<BF16, E8>(wg, jr[r], E, wv[r]);
-      gv[r] = load1<BF16>(g, jr[r]);
-    }
+    if (j0 != rbeg) NR_LOAD_BLOCK(j0)
 #pragma unroll
     for (int t = 0; t < kTPB; ++t) {
       if (t >= ntok) continue;
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(256) void norm_route_kernel(
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int64_t el = (tok0 + t) * d + jr[r];
-        float v = (load1<BF16>(h, el) * inv[t]) * gv[r];
+        float v = (hv[t][r] * inv[t]) * gv[r];
         if constexpr (BF16) {  // x as stored: rounded once to bf16
           const uint32_t b = f32_to_bf16_bits(v);
           if (j0 + 64 * r + lane < rend) static_cast<uint16_t *>(x)[el] = uint16_t(b);
@@ -265,6 +276,7 @@ __global__ __launch_bounds__(256) void norm_route_kernel(
         for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(xv[r], wv[r][e], acc[t][e]);
     }
   }
+#undef NR_LOAD_BLOCK
 
   float mine = 0.f;
 #pragma unroll
