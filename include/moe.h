@@ -31,6 +31,9 @@
  *    blocks x token blocks), MOE_ERR_UNSUPPORTED past it.
  *  - Results are deterministic: no atomics take part in any value, and every
  *    sum has a fixed order.
+ *  - Device memory of the library's own: one read-only 128 KiB row of zeros in
+ *    the code object's static data (the padding rows of the tiled kernels read
+ *    it), present once the library is loaded; no call keeps any state.
  */
 #ifndef MOE_H
 #define MOE_H
