@@ -289,7 +289,8 @@ def main():
     stage = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(4)] for ev in events])
     stage_ms = stage.mean(axis=0)
     norm_ms = float(np.mean([ev[0].elapsed_time(ev[5]) for ev in events])) if args.block else None
-    gpu_ms_step = float(np.mean([ev[0].elapsed_time(ev[4]) for ev in events]))
+    step_ms = np.array([ev[0].elapsed_time(ev[4]) for ev in events])
+    gpu_ms_step = float(np.mean(step_ms))
 
     # one-call API on the same inputs, for comparison (not part of the timed region)
     if args.block:
@@ -432,6 +433,10 @@ def main():
                       "down": round(float(stage_ms[2]), 5),
                       "combine": round(float(stage_ms[3]), 5)},
         "gpu_ms_per_step_events": round(gpu_ms_step, 5),
+        "gpu_ms_per_step_events_stats": {"median": round(float(np.median(step_ms)), 5),
+                                         "min": round(float(np.min(step_ms)), 5),
+                                         "p90": round(float(np.percentile(step_ms, 90)), 5),
+                                         "steps": int(step_ms.size)},
         "block_rmsnorm": None if norm_ms is None else {
             "ms": round(norm_ms, 5),
             "hbm_bytes": T * d * es * 2 + d * es,
