@@ -29,9 +29,15 @@ _DT = {"f32": F32, "bf16": BF16}
 
 
 def build(out: str = LIBRARY, mutant: Optional[int] = None, cc: str = "gcc") -> str:
-    """Compile the oracle (plain C, -O2, no fast-math, no FMA contraction)."""
-    cmd = [cc, "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", "-Wall", "-o", out + ".tmp", SOURCE, "-lm"]
+    """Compile the oracle (plain C, no fast-math, no FMA contraction).
+
+    -O3 without loop vectorisation: the 16 rows of a block that share a weight
+    row are accumulated side by side in vector registers (each row's sum keeps
+    its own ascending order, so the results are those of a scalar build bit for
+    bit); vectorising the loop over the summation index instead would only
+    shuffle registers."""
+    cmd = [cc, "-std=c11", "-O3", "-fno-tree-loop-vectorize", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-o", out + ".tmp", SOURCE, "-lm"]
     if mutant is not None:
         cmd.insert(1, f"-DORACLE_MUTANT={int(mutant)}")
     subprocess.run(cmd, check=True)

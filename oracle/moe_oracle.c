@@ -256,26 +256,32 @@ void oracle_permute_capped(int64_t T, int32_t E, int32_t K, const int32_t *idx, 
   }
 }
 
+#define BLK 16
+
 /*
- * One expert on nb rows (nb small): act[r, j] = silu(g) * u with
- * g = (W1 x_r)_j, u = (W3 x_r)_j; rows given as doubles xr[nb][d].
- * wrow is a d-long scratch row.
+ * One expert on a block of nb <= BLK rows: act[r, j] = silu(g) * u with
+ * g = (W1 x_r)_j, u = (W3 x_r)_j. The rows come interleaved, xt[i * BLK + r] =
+ * x_r[i] (entries of rows r >= nb are zero), so that the BLK dot products that
+ * share one weight row advance side by side; each of them is still its own sum
+ * over i in ascending order. wrow is a d-long scratch row.
  */
-static void gate_up_block(int nb, int64_t d, int64_t h, int dt, const double *xr,
+static void gate_up_block(int nb, int64_t d, int64_t h, int dt, const double *xt,
                           const void *w1e, const void *w3e, double *act, double *wrow) {
   for (int64_t j = 0; j < h; ++j) {
-    double g[16], u[16];
+    double g[BLK], u[BLK];
     for (int64_t i = 0; i < d; ++i) wrow[i] = ld(w1e, dt, (size_t)j * d + i);
-    for (int r = 0; r < nb; ++r) {
-      double s = 0.0;
-      for (int64_t i = 0; i < d; ++i) s += xr[r * d + i] * wrow[i];
-      g[r] = s;
+    for (int r = 0; r < BLK; ++r) g[r] = 0.0;
+    for (int64_t i = 0; i < d; ++i) {
+      const double wv = wrow[i];
+      const double *xi = xt + i * BLK;
+      for (int r = 0; r < BLK; ++r) g[r] += xi[r] * wv;
     }
     for (int64_t i = 0; i < d; ++i) wrow[i] = ld(w3e, dt, (size_t)j * d + i);
-    for (int r = 0; r < nb; ++r) {
-      double s = 0.0;
-      for (int64_t i = 0; i < d; ++i) s += xr[r * d + i] * wrow[i];
-      u[r] = s;
+    for (int r = 0; r < BLK; ++r) u[r] = 0.0;
+    for (int64_t i = 0; i < d; ++i) {
+      const double wv = wrow[i];
+      const double *xi = xt + i * BLK;
+      for (int r = 0; r < BLK; ++r) u[r] += xi[r] * wv;
     }
     for (int r = 0; r < nb; ++r) {
 #if ORACLE_MUTANT == 1
@@ -288,9 +294,15 @@ static void gate_up_block(int nb, int64_t d, int64_t h, int dt, const double *xr
   }
 }
 
-/* out[r, i] = sum_j W2[i, j] * act[r, j] for nb rows; wrow is h-long scratch. */
+/*
+ * out[r, i] = sum_j W2[i, j] * act[r, j] for nb <= BLK rows, each sum over j in
+ * ascending order. at is h * BLK scratch for the rows interleaved as in
+ * gate_up_block; wrow is h-long scratch.
+ */
 static void down_block(int nb, int64_t d, int64_t h, int dt, const double *act,
-                       const void *w2e, double *out, double *wrow) {
+                       const void *w2e, double *out, double *wrow, double *at) {
+  for (int64_t j = 0; j < h; ++j)
+    for (int r = 0; r < BLK; ++r) at[j * BLK + r] = r < nb ? act[r * h + j] : 0.0;
   for (int64_t i = 0; i < d; ++i) {
     for (int64_t j = 0; j < h; ++j) {
 #if ORACLE_MUTANT == 6
@@ -299,15 +311,24 @@ static void down_block(int nb, int64_t d, int64_t h, int dt, const double *act,
       wrow[j] = ld(w2e, dt, (size_t)i * h + j);
 #endif
     }
-    for (int r = 0; r < nb; ++r) {
-      double s = 0.0;
-      for (int64_t j = 0; j < h; ++j) s += wrow[j] * act[r * h + j];
-      out[r * d + i] = s;
+    double s[BLK];
+    for (int r = 0; r < BLK; ++r) s[r] = 0.0;
+    for (int64_t j = 0; j < h; ++j) {
+      const double wv = wrow[j];
+      const double *aj = at + j * BLK;
+      for (int r = 0; r < BLK; ++r) s[r] += wv * aj[r];
     }
+    for (int r = 0; r < nb; ++r) out[r * d + i] = s[r];
   }
 }
 
-#define BLK 16
+/* xt[i * BLK + r] = x_r[i] for the nb rows given by their row pointers' element
+ * offsets into x (dt), zero for r >= nb. */
+static void interleave_rows(int nb, int64_t d, int dt, const void *x, const size_t *row0,
+                            double *xt) {
+  for (int64_t i = 0; i < d; ++i)
+    for (int r = 0; r < BLK; ++r) xt[i * BLK + r] = r < nb ? ld(x, dt, row0[r] + (size_t)i) : 0.0;
+}
 
 /* act[n, h] (double) = silu(W1 x) * (W3 x) for n rows of one expert. */
 void oracle_gate_up(int64_t n, int64_t d, int64_t h, int32_t dt, const void *xrows,
@@ -315,16 +336,17 @@ void oracle_gate_up(int64_t n, int64_t d, int64_t h, int32_t dt, const void *xro
   int64_t nblk = (n + BLK - 1) / BLK;
 #pragma omp parallel
   {
-    double *xr = (double *)malloc(sizeof(double) * BLK * d);
+    double *xt = (double *)malloc(sizeof(double) * BLK * d);
     double *wrow = (double *)malloc(sizeof(double) * d);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t b = 0; b < nblk; ++b) {
       int nb = (int)((n - b * BLK) < BLK ? (n - b * BLK) : BLK);
-      for (int r = 0; r < nb; ++r)
-        for (int64_t i = 0; i < d; ++i) xr[r * d + i] = ld(xrows, dt, (size_t)(b * BLK + r) * d + i);
-      gate_up_block(nb, d, h, dt, xr, w1e, w3e, act + b * BLK * h, wrow);
+      size_t row0[BLK];
+      for (int r = 0; r < nb; ++r) row0[r] = (size_t)(b * BLK + r) * d;
+      interleave_rows(nb, d, dt, xrows, row0, xt);
+      gate_up_block(nb, d, h, dt, xt, w1e, w3e, act + b * BLK * h, wrow);
     }
-    free(xr);
+    free(xt);
     free(wrow);
   }
 }
@@ -336,15 +358,17 @@ void oracle_down(int64_t n, int64_t d, int64_t h, int32_t act_dt, const void *ac
 #pragma omp parallel
   {
     double *a = (double *)malloc(sizeof(double) * BLK * h);
+    double *at = (double *)malloc(sizeof(double) * BLK * h);
     double *wrow = (double *)malloc(sizeof(double) * h);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t b = 0; b < nblk; ++b) {
       int nb = (int)((n - b * BLK) < BLK ? (n - b * BLK) : BLK);
       for (int r = 0; r < nb; ++r)
         for (int64_t j = 0; j < h; ++j) a[r * h + j] = ld(act, act_dt, (size_t)(b * BLK + r) * h + j);
-      down_block(nb, d, h, dt, a, w2e, out + b * BLK * d, wrow);
+      down_block(nb, d, h, dt, a, w2e, out + b * BLK * d, wrow, at);
     }
     free(a);
+    free(at);
     free(wrow);
   }
 }
@@ -387,8 +411,9 @@ void oracle_forward_tokens(int64_t n, const int64_t *tokens, int64_t d, int64_t 
   size_t wsz = (size_t)h * d * esize(dt);
 #pragma omp parallel
   {
-    double *xr = (double *)malloc(sizeof(double) * BLK * d);
+    double *xt = (double *)malloc(sizeof(double) * BLK * d);
     double *act = (double *)malloc(sizeof(double) * BLK * h);
+    double *at = (double *)malloc(sizeof(double) * BLK * h);
     double *ob = (double *)malloc(sizeof(double) * BLK * d);
     double *wrow = (double *)malloc(sizeof(double) * (d > h ? d : h));
 #pragma omp for schedule(dynamic, 1)
@@ -396,20 +421,20 @@ void oracle_forward_tokens(int64_t n, const int64_t *tokens, int64_t d, int64_t 
       int32_t e = bexp[b];
       int64_t s0 = bstart[b];
       int nb = (int)((cnt[e + 1] - s0) < BLK ? (cnt[e + 1] - s0) : BLK);
-      for (int r = 0; r < nb; ++r) {
-        int64_t t = tokens[order[s0 + r] / K];
-        for (int64_t i = 0; i < d; ++i) xr[r * d + i] = ld(x, dt, (size_t)t * d + i);
-      }
+      size_t row0[BLK];
+      for (int r = 0; r < nb; ++r) row0[r] = (size_t)tokens[order[s0 + r] / K] * d;
+      interleave_rows(nb, d, dt, x, row0, xt);
       const char *w1e = (const char *)w1 + (size_t)e * wsz;
       const char *w3e = (const char *)w3 + (size_t)e * wsz;
       const char *w2e = (const char *)w2 + (size_t)e * wsz;
-      gate_up_block(nb, d, h, dt, xr, w1e, w3e, act, wrow);
-      down_block(nb, d, h, dt, act, w2e, ob, wrow);
+      gate_up_block(nb, d, h, dt, xt, w1e, w3e, act, wrow);
+      down_block(nb, d, h, dt, act, w2e, ob, wrow, at);
       for (int r = 0; r < nb; ++r)
         memcpy(obuf + (size_t)order[s0 + r] * d, ob + (size_t)r * d, sizeof(double) * d);
     }
-    free(xr);
+    free(xt);
     free(act);
+    free(at);
     free(ob);
     free(wrow);
   }

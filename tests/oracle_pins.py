@@ -267,6 +267,46 @@ def pin_brute_force_dense_masked_sum(o):
                1e-13, f"brute force {T},{d},{h},{E},{K},{dt}")
 
 
+def pin_blocked_equals_plain_per_token_loop(o):
+    """The oracle evaluates experts over blocks of up to 16 rows that share each
+    weight row; every sum still runs over its own index in ascending order, so
+    its output must equal, bit for bit, a plain per-token evaluation of the
+    output equation (notion page, y = sum_i G(x)_i SwiGLU_i(x) with K nonzero
+    gates) written as scalar float64 loops here. Segments of 20-30 rows per
+    expert span two blocks and a ragged one."""
+    import math
+
+    rng = _rng(16)
+    for (T, d, h, E, K, dt) in ((40, 12, 20, 3, 2, "bf16"), (23, 8, 12, 2, 2, "f32"),
+                                (35, 16, 8, 2, 1, "bf16")):
+        inp = _tiny_layer(rng, T, d, h, E, dt)
+        f = _f64(inp, dt)
+        l, idx, w, _ = o.route(inp["x"], inp["w_g"], K, dt)
+        y = o.forward_tokens(np.arange(T), inp["x"], inp["w1"], inp["w3"], inp["w2"], idx, w,
+                             dt)
+        x = f["x"].tolist()
+        for t in range(T):
+            acc = [0.0] * d
+            for k in range(K):
+                e = int(idx[t, k])
+                w1, w3, w2 = f["w1"][e].tolist(), f["w3"][e].tolist(), f["w2"][e].tolist()
+                a = []
+                for j in range(h):
+                    g = 0.0
+                    u = 0.0
+                    for i in range(d):
+                        g += x[t][i] * w1[j][i]
+                    for i in range(d):
+                        u += x[t][i] * w3[j][i]
+                    a.append(g / (1.0 + math.exp(-g)) * u)
+                for c in range(d):
+                    s = 0.0
+                    for j in range(h):
+                        s += w2[c][j] * a[j]
+                    acc[c] += float(w[t, k]) * s
+            assert np.array_equal(np.array(acc), y[t]), (T, d, h, E, K, dt, t)
+
+
 def pin_hand_examples(o):
     """Hand-derived closed-form examples (tests/golden/hand_examples.json)."""
     with open(GOLDEN) as fh:
