@@ -11,7 +11,10 @@ prefill_8x22b, tiny_f32.
 
 Printed: ONE JSON line with tokens/s, the dominant kernel's roofline fraction
 (HIP events around that kernel inside the timed region) and the CPU oracle
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload. The workloads named by --also
+(default: the 8x7B prefill batch, T = 4096, whose expert GEMMs are bound by the
+matrix cores rather than by HBM) are measured the same way in the same run and
+reported under "sub_workloads" of that line.
 """
 from __future__ import annotations
 
@@ -39,6 +42,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_8x7b")
+    ap.add_argument("--also", default="prefill_8x7b",
+                    help="comma-separated workloads measured after the headline one in the same "
+                         "run and reported as sub-records of its JSON line ('' for none)")
     ap.add_argument("--weight-copies", type=int, default=2,
                     help="rotate this many copies of the expert weights so that no step "
                          "finds them in the 256 MB last-level cache")
@@ -173,6 +179,33 @@ def main():
     if args.sweep:
         return sweep(args)
 
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    out = measure(args.workload, args, args.cpu_seconds)
+    subs = {}
+    for name in [s.strip() for s in args.also.split(",") if s.strip()]:
+        if name == args.workload:
+            continue
+        torch.cuda.empty_cache()
+        rec = measure(name, args, min(args.cpu_seconds, 3.0))
+        for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data",
+                  "unit", "steps", "warmup"):
+            rec.pop(k, None)
+        subs[name] = rec
+    if subs:
+        out["sub_workloads"] = subs
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def measure(workload: str, args, cpu_seconds: float) -> dict:
+    """One workload: warm-up, exactly args.steps timed steps, the dominant kernel's
+    roofline from HIP events inside the timed region, a stage breakdown pass, the
+    one-call entry point, and the CPU oracle on a bounded sample with a parity
+    spot check of the timed run's output."""
     import numpy as np
     import torch
 
@@ -180,10 +213,7 @@ def main():
     import sparse_mixture_experts_wg_amd as moe
     from tests import parity
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    cfg = mi.CONFIGS[args.workload]
+    cfg = mi.CONFIGS[workload]
     T, d, h, E, K, S = cfg.T, cfg.d, cfg.h, cfg.E, cfg.K, cfg.S
     print(f"# workload {cfg.name}: T={T} d={d} h={h} E={E} K={K} {cfg.dtype}; generating",
           file=sys.stderr, flush=True)
@@ -364,7 +394,7 @@ def main():
 
         o = oracle.load()
         per_tok = 2.0 * K * 3 * d * h
-        n = int(min(T, max(8, round(args.cpu_seconds * 2.0e9 * o.threads / per_tok))))
+        n = int(min(T, max(8, round(cpu_seconds * 2.0e9 * o.threads / per_tok))))
         toks = np.arange(n)
         print(f"# CPU oracle on {n} tokens x {o.threads} threads", file=sys.stderr, flush=True)
         c0 = time.perf_counter()
@@ -379,7 +409,7 @@ def main():
             y_ref = o.forward_tokens(toks, xs, inp["w1"], inp["w3"], inp["w2"], idx_r, w_r,
                                      cfg.dtype)
             passes += 1
-            if time.perf_counter() - c0 >= args.cpu_seconds * 0.5 or passes >= 50:
+            if time.perf_counter() - c0 >= cpu_seconds * 0.5 or passes >= 50:
                 break
         cpu_s = (time.perf_counter() - c0) / passes
         cpu = {"value": round(n / cpu_s, 3), "unit": "tokens/s", "cores": o.threads,
@@ -448,8 +478,8 @@ def main():
         "rows_per_expert": counts.tolist(),
         "parity_spot_check": spot,
     }
-    print(json.dumps(out), flush=True)
-    return 0
+    del wsets, dev
+    return out
 
 
 if __name__ == "__main__":

@@ -80,6 +80,14 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 } moe_
  * token's output (the kept weights are not renormalised). A capacity factor cf
  * corresponds to C = ceil(cf * T * K / E). 0 keeps every slot (Mixtral). */
 
+/* Rows per expert of a capacity factor cf = cf_num / cf_den:
+ * C = ceil(cf * T * K / E), in exact integer arithmetic (a float product would
+ * round up one row too many whenever it lands just above an integer, e.g. 1.1 x
+ * 400 / 8). Returns C (a value >= T keeps every slot), or -status when T, K or E
+ * is < 1, K > E, cf_num < 0 or cf_den < 1 (MOE_ERR_SHAPE), or C does not fit an
+ * int32 (MOE_ERR_UNSUPPORTED). Host only. */
+int64_t moe_capacity_rows(int64_t T, int32_t K, int32_t E, int64_t cf_num, int64_t cf_den);
+
 /* moe_problem.flags bits.
  * MOE_FLAG_DOWN_PARTIALS: the caller lets moe_expert_down / moe_expert_swiglu
  *   split the sum over h into moe_down_parts(p) float32 partial sums, stored one
@@ -184,7 +192,10 @@ moe_status moe_expert_gate_up_rows(const moe_problem *p, const void *x, const in
 
 /*
  * Expert down projection: o_perm[r] = W2_e act[r] for every expert's segment,
- * accumulated and stored in float32.
+ * accumulated and stored in float32 -- the outer matrix of the SwiGLU expert
+ * (notion page, "Implementation": SwiGLU experts; SwiGLU_e(x) =
+ * W2_e (silu(W1_e x) * W3_e x)), applied to the activations moe_expert_gate_up
+ * wrote.
  *   act     [S, h]     dtype
  *   offsets [E + 1]    int32 (as above)
  *   w2      [E, d, h]  dtype
@@ -200,6 +211,8 @@ size_t moe_expert_workspace_bytes(const moe_problem *p);
 
 /*
  * Both expert projections: o_perm[r] = SwiGLU_e(x_perm[r]) for every segment,
+ * the expert function E_i of the output equation (notion page, "Architectural
+ * details", y = sum_i G(x)_i E_i(x), with the SwiGLU experts of "Implementation"),
  * with the hidden activations in `ws` (at least moe_expert_workspace_bytes);
  * o_perm as for moe_expert_down.
  */
@@ -263,7 +276,10 @@ moe_status moe_block_forward(const moe_problem *p, const void *h, const void *no
 size_t moe_forward_workspace_bytes(const moe_problem *p);
 
 /*
- * The whole layer: route -> permute -> gate-up -> down -> combine on `stream`.
+ * The whole layer: route -> permute -> gate-up -> down -> combine on `stream`,
+ * i.e. y = sum_i G(x)_i SwiGLU_i(x) with G(x) = Softmax(Top2(x . W_g)) (notion
+ * page, "Architectural details": sparse-gating and output equations; crackai
+ * page, "Top-2 Routing in Detail": y = w_1 Expert_i1(x) + w_2 Expert_i2(x)).
  *   x [T, d], w_g [d, E], w1/w3 [E, h, d], w2 [E, d, h] in dtype
  *   y [T, d] out_dtype out
  *   topk_idx [T, K] int32 and topk_w [T, K] float32: optional outputs (NULL to

@@ -7,9 +7,10 @@ kernels in libmoe.so behind the C ABI of include/moe.h; this package is the
 Python binding (torch tensors in, torch tensors out).
 """
 from .binding import (  # noqa: F401
-    BF16, F32, FLAG_DOWN_PARTIALS, PATH_AUTO, PATH_STREAM, PATH_TILED, MoeError, Problem,
-    block_forward, block_workspace_bytes, capacity_rows, combine, combine_residual, down_parts, expert_down,
-    expert_gate_up, expert_gate_up_rows, expert_swiglu, expert_workspace_bytes, forward, forward_workspace_bytes,
+    BF16, F32, FLAG_DOWN_PARTIALS, PATH_AUTO, PATH_STREAM, PATH_TILED,
+    MoeError, Problem, block_forward, block_workspace_bytes, capacity_rows, combine,
+    combine_residual, down_parts, expert_down, expert_gate_up, expert_gate_up_rows,
+    expert_swiglu, expert_workspace_bytes, forward, forward_workspace_bytes,
     header_functions, last_error, lib, permute, problem, resolve_path, rmsnorm, route,
     status_string,
 )

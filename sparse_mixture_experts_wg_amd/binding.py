@@ -49,11 +49,23 @@ def problem(T: int, d: int, h: int, E: int = 8, K: int = 2, dtype: str = "bf16",
                    capacity, 0)
 
 
-def capacity_rows(T: int, K: int, E: int, capacity_factor: float) -> int:
-    """Rows per expert for a capacity factor: ceil(cf * T * K / E)."""
-    import math
+def capacity_rows(T: int, K: int, E: int, capacity_factor) -> int:
+    """Rows per expert for a capacity factor, ceil(cf * T * K / E), computed by the
+    library in exact integer arithmetic. cf is taken as the exact rational of its
+    decimal text (1.1 means 11/10), or given as a fractions.Fraction or a
+    (numerator, denominator) pair."""
+    from fractions import Fraction
 
-    return int(math.ceil(capacity_factor * T * K / E))
+    if isinstance(capacity_factor, tuple):
+        cf = Fraction(int(capacity_factor[0]), int(capacity_factor[1]))
+    elif isinstance(capacity_factor, Fraction):
+        cf = capacity_factor
+    else:
+        cf = Fraction(repr(float(capacity_factor)))
+    n = lib.moe_capacity_rows(int(T), int(K), int(E), cf.numerator, cf.denominator)
+    if n < 0:
+        raise MoeError(-n, last_error())
+    return int(n)
 
 
 def header_functions(path: str = HEADER):
@@ -77,6 +89,8 @@ def _load() -> ctypes.CDLL:
     sz = ctypes.c_size_t
     sig = {
         "moe_status_string": ([i32], ctypes.c_char_p),
+        "moe_capacity_rows": ([ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                               ctypes.c_int64], ctypes.c_int64),
         "moe_last_error": ([], ctypes.c_char_p),
         "moe_resolve_path": ([P], i32),
         "moe_down_parts": ([P], i32),
@@ -355,3 +369,4 @@ def forward(p: Problem, x, w_g, w1, w3, w2, y=None, topk_idx=None, topk_w=None, 
                            _ptr(topk_w, "topk_w", (T, K), torch.float32), _ptr(ws, "ws"),
                            ws.numel() * ws.element_size(), _stream(stream)))
     return y
+

@@ -10,6 +10,7 @@
 #include <cstring>
 #include <exception>
 
+#include "abi_internal.h"
 #include "kernels.h"
 
 namespace {
@@ -28,6 +29,19 @@ moe_status ok() {
   g_err[0] = '\0';
   return MOE_OK;
 }
+
+}  // namespace
+
+// Error reporting for the library's other host sources (abi_internal.h).
+moe_status moe::set_error(moe_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
@@ -186,7 +200,9 @@ ForwardLayout forward_layout(const moe_problem *p) {
   L.offsets = take(size_t(p->E + 1) * 4);
   L.perm = take(S * 4);
   L.slot = take(S * 4);
-  L.x_perm = take(S * p->d * esize(p->dtype));
+  // float32 problems gather the token rows into x_perm; the bf16 gate-up reads
+  // them through perm_token and needs no copy
+  L.x_perm = p->dtype == MOE_F32 ? take(S * p->d * esize(p->dtype)) : 0;
   L.act = take(S * p->h * esize(p->dtype));
   moe_problem q = *p;
   q.flags |= MOE_FLAG_DOWN_PARTIALS;  // the layer's own o_perm may hold partials
@@ -323,7 +339,7 @@ moe_status run_layer(const moe_problem *p, const void *x, const void *w_g, const
   int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
   int32_t *perm = reinterpret_cast<int32_t *>(base + L.perm);
   int32_t *slot = reinterpret_cast<int32_t *>(base + L.slot);
-  void *x_perm = base + L.x_perm;
+  void *x_perm = p->dtype == MOE_F32 ? base + L.x_perm : nullptr;
   void *act = base + L.act;
   float *o_perm = reinterpret_cast<float *>(base + L.o_perm);
   const hipStream_t s = as_stream(stream);
@@ -366,6 +382,28 @@ const char *moe_status_string(int status) {
 }
 
 const char *moe_last_error(void) { return g_err; }
+
+int64_t moe_capacity_rows(int64_t T, int32_t K, int32_t E, int64_t cf_num, int64_t cf_den) {
+  if (T < 1 || K < 1 || E < 1 || K > E) {
+    fail(MOE_ERR_SHAPE, "T=%lld K=%d E=%d: every size must be >= 1 and K <= E", (long long)T, K, E);
+    return -int64_t(MOE_ERR_SHAPE);
+  }
+  if (cf_num < 0 || cf_den < 1) {
+    fail(MOE_ERR_SHAPE, "capacity factor %lld/%lld: need num >= 0 and den >= 1",
+         (long long)cf_num, (long long)cf_den);
+    return -int64_t(MOE_ERR_SHAPE);
+  }
+  // ceil(num * T * K / (den * E)) in exact integer arithmetic
+  const unsigned __int128 n = (unsigned __int128)cf_num * uint64_t(T) * uint64_t(K);
+  const unsigned __int128 q = (unsigned __int128)cf_den * uint64_t(E);
+  const unsigned __int128 c = (n + q - 1) / q;
+  if (c > (unsigned __int128)INT32_MAX) {
+    fail(MOE_ERR_UNSUPPORTED, "capacity %s rows does not fit moe_problem.capacity", "> 2^31 - 1");
+    return -int64_t(MOE_ERR_UNSUPPORTED);
+  }
+  ok();
+  return int64_t(c);
+}
 
 int moe_down_parts(const moe_problem *p) {
   const moe_status st = check_problem(p);

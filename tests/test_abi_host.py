@@ -113,6 +113,31 @@ def test_capacity_field():
     assert ctypes.sizeof(binding.Problem) == 56
 
 
+def test_capacity_rows_exact():
+    """C = ceil(cf * T * K / E) in exact arithmetic: a float product lands just above
+    the integer for 1.1 x 400 x 2 / 8 = 110 (and 1.1 x 200 x 2 / 8 = 55) and would
+    keep one row too many."""
+    assert moe.capacity_rows(200, 2, 8, 1.1) == 55
+    assert moe.capacity_rows(400, 2, 8, 1.1) == 110
+    assert moe.capacity_rows(400, 2, 8, (11, 10)) == 110
+    assert moe.capacity_rows(401, 2, 8, (11, 10)) == 111  # 110.275 rounds up
+    assert moe.capacity_rows(7, 1, 3, 1.0) == 3           # ceil(7 / 3)
+    assert moe.capacity_rows(4096, 2, 8, 0.0) == 0
+    # every case with K = 2, E = 8 and T < 5000 against exact rational arithmetic
+    from fractions import Fraction
+    for cf in ("0.5", "0.9", "1.0", "1.1", "1.2", "1.25", "1.3", "1.5", "2.0", "3.3"):
+        q = Fraction(cf)
+        for T in range(1, 5000, 7):
+            want = -(-(q.numerator * T * 2) // (q.denominator * 8))
+            assert moe.capacity_rows(T, 2, 8, float(cf)) == want, (cf, T)
+    for args in ((0, 2, 8, 1, 1), (10, 0, 8, 1, 1), (10, 3, 2, 1, 1), (10, 2, 8, -1, 1),
+                 (10, 2, 8, 1, 0)):
+        assert lib.moe_capacity_rows(*args) == -binding.ERR_SHAPE, args
+    assert lib.moe_capacity_rows(1 << 26, 2, 2, 1 << 20, 1) == -binding.ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError):
+        moe.capacity_rows(0, 2, 8, 1.0)
+
+
 def test_down_parts():
     """Partial sums only when asked for, on the tiled bf16 path: 4 parts when they all fit
     one round of workgroups, 1 from 8 rounds on, else 2; a part needs an even count of
@@ -131,7 +156,7 @@ def test_down_parts():
     assert moe.down_parts(_p(T=64, d=128, h=256, dtype="f32", flags=P)) == 1
     # the layer's own workspace makes room for the partial sums it uses
     S, d, h = 4096 * 2, 4096, 14336
-    acts = S * d * 2 + S * h * 2  # x_perm and act, bf16
+    acts = S * h * 2  # act, bf16 (no x_perm: the bf16 gate-up reads x through perm_token)
     assert moe.forward_workspace_bytes(_p(T=4096, d=d, h=h)) >= acts + 2 * S * d * 4
     with pytest.raises(moe.MoeError):
         moe.down_parts(_p(T=0))
@@ -179,8 +204,21 @@ def test_workspace_sizes_and_too_small():
     p = _p(T=100, d=256, h=512, E=8, K=2)
     S = 200
     need = moe.forward_workspace_bytes(p)
-    # x_perm + act (bf16) + o_perm (f32) + 4 int/float index arrays + offsets, 256-B aligned
-    assert need >= S * 256 * 2 + S * 512 * 2 + S * 256 * 4 + 4 * S * 4
+
+    def a256(n):
+        return (n + 255) // 256 * 256
+    # bf16: act (bf16) + o_perm (f32, with the partial sums the layer lets the down
+    # projection leave) + 4 int/float index arrays + offsets, each piece 256-B aligned;
+    # no x_perm (the gate-up reads the token rows through perm_token)
+    parts = moe.down_parts(_p(T=100, d=256, h=512, flags=binding.FLAG_DOWN_PARTIALS))
+    assert parts == 4
+    assert need == (4 * a256(S * 4) + a256(9 * 4) + a256(S * 512 * 2) +
+                    a256(parts * S * 256 * 4))
+    # float32 gathers x_perm [S, d] as well (and never splits the down projection)
+    f32p = _p(T=100, d=256, h=512, E=8, K=2, dtype="f32")
+    assert moe.forward_workspace_bytes(f32p) == (4 * a256(S * 4) + a256(9 * 4) +
+                                                 a256(S * 256 * 4) + a256(S * 512 * 4) +
+                                                 a256(S * 256 * 4))
     assert need % 256 == 0
     assert moe.expert_workspace_bytes(p) == S * 512 * 2
     st = lib.moe_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,

@@ -1,9 +1,11 @@
 """GPU parity: every step of the HIP path against the CPU oracle on the same
 seeded inputs, through the C ABI (via the thin binding).
 
-Small shapes are compared in full; the full-size workloads compare the routing
-of every token and the layer output on a seeded sample of tokens (first and last
-token always included, plus every token whose set differs from the oracle's).
+Small shapes are compared in full. The full-size workloads compare the routing of
+every token; the layer output of every token up to the 4096-token prefill batch,
+and at the two largest workloads of every token whose rows sit at a tile edge of
+the expert projections plus random ones (and every token whose set differs from
+the oracle's).
 """
 import numpy as np
 import pytest
@@ -199,7 +201,30 @@ def test_skewed_routing_empty_experts(moe, oracle):
 # ---- the five workloads ----------------------------------------------------------
 
 WORKLOADS = ["tiny_f32", "decode_8x7b", "prefill_8x7b", "skew_8x7b", "prefill_8x22b"]
-SAMPLE = 40
+# workloads whose every token is compared; the two largest compare a sample that
+# reaches every tile edge (below)
+FULL = {"tiny_f32", "decode_8x7b", "prefill_8x7b"}
+RANDOM_EXTRA = 256
+
+
+def _tile_edge_tokens(idx, E, oracle, T, seed=0):
+    """Tokens whose rows sit at a tile edge of the expert projections, from the
+    routing's own segments (offsets and row -> token map of the stable sort): in
+    every expert segment the first and last row of each 32-row block (every token
+    tile, 64, 128 or 256 rows, starts and ends on such a row, and so does every
+    wavefront's share of one) and the segment's last two rows, plus RANDOM_EXTRA
+    random tokens."""
+    off, perm, _ = oracle.permute(idx, E)
+    rows = []
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        r = np.arange(a, b)
+        j = r - a
+        rows.append(r[(j % 32 == 0) | (j % 32 == 31) | (r >= b - 2)])
+    toks = np.unique(perm[np.concatenate(rows)])
+    return np.union1d(toks, parity.sample_tokens(T, RANDOM_EXTRA, seed=seed)).astype(np.int64)
 
 
 @pytest.mark.parametrize("name", WORKLOADS)
@@ -213,8 +238,11 @@ def test_forward_workload(moe, oracle, name):
     y_st = _run_staged_as_bench(moe, cfg, dev)
     del dev
     assert np.array_equal(y_st, y), "staged steps differ from moe_forward"
-    toks = parity.sample_tokens(cfg.T, SAMPLE if cfg.T > 64 else cfg.T, seed=0)
-    _say(f"  oracle on {len(toks)} tokens")
+    if name in FULL:
+        toks = np.arange(cfg.T)
+    else:
+        toks = _tile_edge_tokens(idx, cfg.E, oracle, cfg.T)
+    _say(f"  oracle on {len(toks)} of {cfg.T} tokens")
     toks, y_ref, diff, margin = _layer_ref(oracle, inp, cfg, toks, idx, w)
     rel = parity.check_output(y[toks], y_ref, cfg.dtype, name)
     counts = np.bincount(idx.reshape(-1), minlength=cfg.E)
@@ -472,12 +500,16 @@ def test_expert_steps(moe, oracle, name, path, T, d, h, counts, flags, parts_exp
     o = moe.expert_down(p, parity.device_array(act_in, "bf16"), dev_off, w2)
     o_full = moe.expert_swiglu(p, dev_x, dev_off, w1, w3, w2)
     torch.cuda.synchronize()
-    act_h = mi.bf16_bits_to_f32(parity.host_array(act)).astype(np.float64)
+    # rows at and past offsets[E] are never written: read only the rows below it
+    n = int(off[-1])
+    act_h = mi.bf16_bits_to_f32(parity.host_array(act)[:n]).astype(np.float64)
     o_h = parity.host_array(o).astype(np.float64)
     of_h = parity.host_array(o_full).astype(np.float64)
     if parts > 1:  # [parts, S, d] partial sums over h; the row is their sum
-        o_h = o_h.reshape(parts, S, d).sum(axis=0)
-        of_h = of_h.reshape(parts, S, d).sum(axis=0)
+        o_h = o_h.reshape(parts, S, d)[:, :n].sum(axis=0)
+        of_h = of_h.reshape(parts, S, d)[:, :n].sum(axis=0)
+    else:
+        o_h, of_h = o_h[:n], of_h[:n]
     for e in range(E):
         a, b = off[e], off[e + 1]
         if a == b:
