@@ -31,9 +31,11 @@
  *    blocks x token blocks), MOE_ERR_UNSUPPORTED past it.
  *  - Results are deterministic: no atomics take part in any value, and every
  *    sum has a fixed order.
- *  - Device memory of the library's own: one read-only 128 KiB row of zeros in
- *    the code object's static data (the padding rows of the tiled kernels read
- *    it), present once the library is loaded; no call keeps any state.
+ *  - Device memory of the library's own, in the code objects' static data and
+ *    present on a GPU once the library is loaded there: one read-only 128 KiB
+ *    row of zeros (the padding rows of the tiled kernels read it) and the
+ *    MOE_NOALLOC_SCRATCH_BYTES scratch array of moe_forward_noalloc. No other
+ *    call keeps any state.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -289,6 +291,27 @@ size_t moe_forward_workspace_bytes(const moe_problem *p);
 moe_status moe_forward(const moe_problem *p, const void *x, const void *w_g, const void *w1,
                        const void *w3, const void *w2, void *y, int32_t *topk_idx,
                        float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/* Size of the static scratch array moe_forward_noalloc uses as its workspace. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * moe_forward for callers that cannot allocate device memory (code under
+ * stream capture, serving loops, harnesses that forbid hipMalloc): the same
+ * layer, bitwise the same results, with the workspace taken from a static
+ * device array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU holds from
+ * the library's load until the process ends. No call allocates or frees
+ * anything. Problems whose moe_forward_workspace_bytes exceeds that size are
+ * rejected with MOE_ERR_WORKSPACE (at d = 4096, h = 14336, E = 8, K = 2 this
+ * admits a few hundred tokens, decode batches included). Every call on one GPU
+ * uses that GPU's one array: calls that overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller. The array's
+ * device address is looked up on the first call on each device (with that
+ * device current). Arguments as for moe_forward, without ws and ws_bytes.
+ */
+moe_status moe_forward_noalloc(const moe_problem *p, const void *x, const void *w_g,
+                               const void *w1, const void *w3, const void *w2, void *y,
+                               int32_t *topk_idx, float *topk_w, void *stream);
 
 #ifdef __cplusplus
 }

@@ -91,6 +91,7 @@ def _load() -> ctypes.CDLL:
         "moe_status_string": ([i32], ctypes.c_char_p),
         "moe_capacity_rows": ([ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                ctypes.c_int64], ctypes.c_int64),
+        "moe_forward_noalloc": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
         "moe_last_error": ([], ctypes.c_char_p),
         "moe_resolve_path": ([P], i32),
         "moe_down_parts": ([P], i32),
@@ -370,3 +371,24 @@ def forward(p: Problem, x, w_g, w1, w3, w2, y=None, topk_idx=None, topk_w=None, 
                            ws.numel() * ws.element_size(), _stream(stream)))
     return y
 
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(p: Problem, x, w_g, w1, w3, w2, y=None, topk_idx=None, topk_w=None,
+                    stream=None):
+    """moe_forward_noalloc: the whole layer with the library's static scratch array
+    as its workspace (no device allocation by the library)."""
+    torch = _torch()
+    T, d, h, E, K = int(p.T), int(p.d), int(p.h), int(p.E), int(p.K)
+    dt = _tdtype(p.dtype)
+    yd = _tdtype(p.out_dtype)
+    y = _empty((T, d), yd, x) if y is None else y
+    _check(lib.moe_forward_noalloc(ctypes.byref(p), _ptr(x, "x", (T, d), dt),
+                                   _ptr(w_g, "w_g", (d, E), dt), _ptr(w1, "w1", (E, h, d), dt),
+                                   _ptr(w3, "w3", (E, h, d), dt), _ptr(w2, "w2", (E, d, h), dt),
+                                   _ptr(y, "y", (T, d), yd),
+                                   _ptr(topk_idx, "topk_idx", (T, K), torch.int32),
+                                   _ptr(topk_w, "topk_w", (T, K), torch.float32),
+                                   _stream(stream)))
+    return y

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libmoe.so")
 
 ARCH = "gfx950"
-SOURCES = ["abi.cpp", "norm.hip", "route.hip", "permute.hip", "combine.hip", "gemm_f32.hip",
+SOURCES = ["abi.cpp", "noalloc.hip", "norm.hip", "route.hip", "permute.hip", "combine.hip", "gemm_f32.hip",
            "gemm_stream.hip", "gemm_tiled.hip"]
 
 
