@@ -54,9 +54,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kZeroK = 65536;
 __device__ __attribute__((aligned(1024))) uint16_t g_zero_row[kZeroK];
 
-// s_waitcnt immediates: vmcnt(0) / vmcnt(4) with the other counters at their maximum.
+// s_waitcnt immediates (vmcnt in bits 3:0, expcnt 6:4, lgkmcnt 11:8): vmcnt(n)
+// with the other counters at their maximum, and vmcnt(n) with lgkmcnt(0).
 constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm4 = 0x0F74;
+constexpr int kWaitVm0Lgkm0 = 0x0070;
+// vmcnt(n), n < 64 (its upper two bits go to bits 15:14)
+constexpr int wait_vm(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+constexpr int wait_vm_lgkm0(int n) { return ((n >> 4) << 14) | 0x0070 | (n & 15); }
 
 // Workgroup barrier without the fence of __syncthreads() (which would wait for
 // every copy in flight); the explicit vmcnt waits before it are the ones the
@@ -67,6 +71,95 @@ constexpr int kWaitVm4 = 0x0F74;
     __builtin_amdgcn_s_barrier();        \
     asm volatile("" ::: "memory");       \
   }
+
+// ---- the main loop shared by the kernels below ---------------------------------
+// A wavefront owns FA x FB accumulators of 32 x 32 (FA fragments of 32 weight rows,
+// FB of 32 tokens). A 64-wide k-block is four 16-wide k-steps. Fragments of k-step
+// kk are read from LDS one k-step ahead into the other of two register buffers.
+// With copies into LDS in flight the compiler can only wait for every LDS read at
+// once (lgkmcnt(0)), so the order within a k-step is fixed explicitly: the first
+// MFMA, then the next k-step's reads, then the other MFMAs. The wait in front of
+// a k-step's first MFMA then only covers reads issued a whole k-step earlier
+// (measured on MI355X: with the reads issued before the first MFMA, or spread
+// among the MFMAs, the last reads were still in flight at that wait).
+#define TL_READ(SW, SX, KK, BUF)                                                           \
+  {                                                                                        \
+    const char *pa_ = reinterpret_cast<const char *>(SW) + baseA;                          \
+    const char *pb_ = reinterpret_cast<const char *>(SX) + baseB;                          \
+    _Pragma("unroll") for (int f = 0; f < FA; ++f) fa[BUF][f] =                            \
+        *reinterpret_cast<const bf16x8 *>(pa_ + f * 4096 + offk[KK]);                      \
+    _Pragma("unroll") for (int t = 0; t < FB; ++t) fb[BUF][t] =                            \
+        *reinterpret_cast<const bf16x8 *>(pb_ + t * 4096 + offk[KK]);                      \
+  }
+#define TL_MFMA(BUF)                                                                       \
+  _Pragma("unroll") for (int t = 0; t < FB; ++t)                                           \
+    _Pragma("unroll") for (int f = 0; f < FA; ++f)                                         \
+      acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[BUF][f], fb[BUF][t], acc[f][t], \
+                                                          0, 0, 0);
+// multiply the fragments in BUF while k-step KKN of (SW, SX) is read into BUFN
+#define TL_KSTEP(SW, SX, KKN, BUFN, BUF)                                                   \
+  TL_READ(SW, SX, KKN, BUFN)                                                               \
+  TL_MFMA(BUF)                                                                             \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x100, FA + FB, 0);                                 \
+  __builtin_amdgcn_sched_group_barrier(0x008, FA * FB - 1, 0);                             \
+  __builtin_amdgcn_sched_barrier(0);
+// the last k-step of a k-block, no reads behind it
+#define TL_KLAST(BUF)                                                                      \
+  TL_MFMA(BUF)                                                                             \
+  __builtin_amdgcn_sched_barrier(0);
+// Three weight stages and two token stages (weights of k-block KB in slot KB % 3,
+// tokens in KB % 2; WS/XS the slots of KB, WN/XN those of KB + 1). The barrier sits
+// before the last k-step: k-steps 0-2 of KB are multiplied, the wavefront waits for
+// its fragment reads and for the copies of KB + 1 (kStepWait: all but the weight
+// copies of KB + 2, the youngest), the barrier makes every wavefront's copies visible and
+// frees KB's slots, the copies of KB + 2 (tokens) and KB + 3 (weights) go into them,
+// and k-step 3 of KB is multiplied from registers while k-step 0 of KB + 1 is read:
+// the matrix cores do not drain at the barrier (5-8% faster than a barrier after
+// the last k-step, bitwise the same sums). Weights are fetched about two k-blocks
+// ahead, tokens one.
+#define TL_STEP(KB, WS, XS, WN, XN)                                                        \
+  TL_KSTEP(sW##WS, sX##XS, 1, 1, 0)                                                        \
+  TL_KSTEP(sW##WS, sX##XS, 2, 0, 1)                                                        \
+  TL_KSTEP(sW##WS, sX##XS, 3, 1, 0)                                                        \
+  __builtin_amdgcn_s_waitcnt(kStepWait);                                                   \
+  TILED_BARRIER()                                                                          \
+  DMAX(sX##XS, (KB) + 2)                                                                   \
+  DMAW(sW##WS, (KB) + 3)                                                                   \
+  TL_KSTEP(sW##WN, sX##XN, 0, 0, 1)
+// The whole k-loop over nk (even) k-blocks with that pipeline; unrolled by 6 so
+// that every slot index is static.
+#define TL_KLOOP(PROLOGUE_WAIT)                                                            \
+  DMAW(sW0, 0)                                                                             \
+  DMAX(sX0, 0)                                                                             \
+  DMAW(sW1, 1)                                                                             \
+  DMAX(sX1, 1)                                                                             \
+  DMAW(sW2, 2)                                                                             \
+  __builtin_amdgcn_s_waitcnt(PROLOGUE_WAIT); /* k-block 0 has landed */                    \
+  TILED_BARRIER()                                                                          \
+  TL_READ(sW0, sX0, 0, 0)                                                                  \
+  {                                                                                        \
+    int kt = 0;                                                                            \
+    for (; kt + 6 <= nk; kt += 6) {                                                        \
+      TL_STEP(kt + 0, 0, 0, 1, 1)                                                          \
+      TL_STEP(kt + 1, 1, 1, 2, 0)                                                          \
+      TL_STEP(kt + 2, 2, 0, 0, 1)                                                          \
+      TL_STEP(kt + 3, 0, 1, 1, 0)                                                          \
+      TL_STEP(kt + 4, 1, 0, 2, 1)                                                          \
+      TL_STEP(kt + 5, 2, 1, 0, 0)                                                          \
+    }                                                                                      \
+    if (kt < nk) { /* 2 or 4 k-blocks remain */                                            \
+      TL_STEP(kt + 0, 0, 0, 1, 1)                                                          \
+      TL_STEP(kt + 1, 1, 1, 2, 0)                                                          \
+      kt += 2;                                                                             \
+    }                                                                                      \
+    if (kt < nk) {                                                                         \
+      TL_STEP(kt + 0, 2, 0, 0, 1)                                                          \
+      TL_STEP(kt + 1, 0, 1, 1, 0)                                                          \
+    }                                                                                      \
+  }                                                                                        \
+  /* no copy or read in flight past the loop (the last step read ahead) */                 \
+  __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
 
 // Physical 16-byte chunk = logical chunk ^ swz(row); depends on row & 31 only.
 __device__ __forceinline__ int swz(int r) { return ((r & 31) ^ ((r & 31) >> 3)) & 7; }
@@ -83,11 +176,50 @@ __device__ __forceinline__ void dma16_nt(const uint16_t *g, lds_void *l) {
 }
 
 // The tile of this workgroup: expert e (rows row0 .. row0 + ne - 1), token
-// block m0, output column c0 and, with ksplit > 1 (down only), the part ks of
-// the sum over K. False when the workgroup has no tile.
+// block m0 of bt tokens, output column c0 and, with ksplit > 1 (down only), the
+// part ks of the sum over K. False when the workgroup has no tile.
 struct Tile {
-  int e, row0, ne, m0, c0, ks;
+  int e, row0, ne, m0, c0, ks, bt;
 };
+
+// Width of the last token tile of an expert whose rows leave `rem` (1-255) past
+// its full 256-token tiles: the narrowest of 64, 128, 256 that holds them.
+__device__ __forceinline__ int tail_width(int rem) { return rem <= 64 ? 64 : rem <= 128 ? 128 : 256; }
+
+// Tiles of 256 tokens, except that each expert's last, partly filled token tile
+// is only as wide as tail_width(rows % 256): the matrix work spent on rows past
+// an expert's end shrinks from up to 255 rows to at most 63 (at the 8x7B prefill
+// shape, 33 instead of 36 full tiles' worth). Order and XCD mapping as
+// find_tile.
+template <int kCols>
+__device__ __forceinline__ bool find_tile_mixed(const int32_t *__restrict__ offsets, int E, int N,
+                                                int ksplit, int min_tail, Tile &tl) {
+  const int ct = (N + kCols - 1) / kCols;
+  int total = 0;
+  for (int q = 0; q < E; ++q) total += ct * ((offsets[q + 1] - offsets[q] + 255) / 256);
+  const int g8 = (total * ksplit + kXCD - 1) / kXCD;
+  const int b = blockIdx.x;
+  if (b >= g8 * kXCD) return false;
+  int L = (b % kXCD) * g8 + b / kXCD;
+  if (L >= total * ksplit) return false;
+  tl.ks = L / total;
+  L -= tl.ks * total;
+  int e = 0, row0 = 0, ne = 0, mtiles = 0;
+  for (; e < E; ++e) {
+    row0 = offsets[e];
+    ne = offsets[e + 1] - row0;
+    mtiles = (ne + 255) / 256;
+    if (L < ct * mtiles) break;
+    L -= ct * mtiles;
+  }
+  tl.e = e;
+  tl.row0 = row0;
+  tl.ne = ne;
+  tl.m0 = (L % mtiles) * 256;
+  tl.c0 = (L / mtiles) * kCols;
+  tl.bt = ne - tl.m0 >= 256 ? 256 : max(tail_width(ne - tl.m0), min_tail);
+  return true;
+}
 template <int BT, int kCols>
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int N,
                                           int ksplit, Tile &tl) {
@@ -114,21 +246,22 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
   tl.ne = ne;
   tl.m0 = (L % mtiles) * BT;
   tl.c0 = (L / mtiles) * kCols;
+  tl.bt = BT;
   return true;
 }
 
-// Epilogue of the 2 x 4 wavefront grid (BT = 256): lane holds token column j = lane & 31
-// and weight rows i = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4) of each 32x32
-// fragment; gate-up fragments 0, 1 are g and 2, 3 the u of the same columns.
-template <bool GATEUP, int BT>
-__device__ __forceinline__ void store_2x4(const f32x16 (&acc)[4][BT / 128], const Tile &tl,
-                                          int lane, int wr, int wc, int N,
-                                          int64_t part_stride, void *__restrict__ out) {
-  constexpr int NT = BT / 128;
+// Epilogue of a wavefront that owns 128 weight rows (wr) x NT * 32 tokens from
+// token `tok0` of its tile: lane holds token column j = lane & 31 and weight rows
+// i = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4) of each 32x32 fragment; gate-up
+// fragments 0, 1 are g and 2, 3 the u of the same columns.
+template <bool GATEUP, int NT>
+__device__ __forceinline__ void store_128rows(const f32x16 (&acc)[4][NT], const Tile &tl,
+                                              int lane, int wr, int tok0, int N,
+                                              int64_t part_stride, void *__restrict__ out) {
   const int ih = 4 * (lane >> 5);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int tok = tl.m0 + wc * (BT / 4) + t * 32 + (lane & 31);
+    const int tok = tl.m0 + tok0 + t * 32 + (lane & 31);
     if (tok >= tl.ne) continue;
     const size_t orow = size_t(tl.row0 + tok) * N + size_t(tl.ks) * size_t(part_stride);
     if constexpr (GATEUP) {
@@ -163,34 +296,22 @@ __device__ __forceinline__ void store_2x4(const f32x16 (&acc)[4][BT / 128], cons
   }
 }
 
-// BT = 256: three weight stages and two token stages (160 KiB of LDS). Per
-// k-block: the token tile one k-block ahead and the weight tile two k-blocks
-// ahead are issued, the current k-block is multiplied, then a wait for all but
-// the 4 youngest copies (the weights two ahead) and a barrier. The weight tile
-// of the first token block to reach a k-block is an HBM miss; two k-blocks of
-// lead hide more of that latency than one (measured 4-9% faster than two
-// stages of both).
+// BT = 256: three weight stages and two token stages (160 KiB of LDS), the
+// pipeline of TL_KLOOP. The weight tile of the first token block to reach a
+// k-block is an HBM miss; about two k-blocks of lead hide more of that latency
+// than one (measured 4-9% faster than two stages of both).
 template <bool GATEUP>
-__global__ __launch_bounds__(512) void tiled256_kernel(const uint16_t *__restrict__ X,
-                                                       const int32_t *__restrict__ offsets, int E,
-                                                       const uint16_t *__restrict__ Wa,
-                                                       const uint16_t *__restrict__ Wb,
-                                                       void *__restrict__ out, int N, int K,
-                                                       int ksplit, int64_t part_stride,
-                                                       const int32_t *__restrict__ rowmap) {
-  constexpr int BT = 256;
-  Tile tl;
-  if (!find_tile<BT, GATEUP ? 128 : 256>(offsets, E, N, ksplit, tl)) return;
+__device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restrict__ X,
+                                        const uint16_t *__restrict__ Wa,
+                                        const uint16_t *__restrict__ Wb, void *__restrict__ out,
+                                        int N, int K, int ksplit, int64_t part_stride,
+                                        const int32_t *__restrict__ rowmap, uint16_t *sW0,
+                                        uint16_t *sW1, uint16_t *sW2, uint16_t *sX0,
+                                        uint16_t *sX1) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wr = wave >> 2, wc = wave & 3;
-
-  __shared__ __attribute__((aligned(1024))) uint16_t sW0[256 * 64];
-  __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
-  __shared__ __attribute__((aligned(1024))) uint16_t sW2[256 * 64];
-  __shared__ __attribute__((aligned(1024))) uint16_t sX0[256 * 64];
-  __shared__ __attribute__((aligned(1024))) uint16_t sX1[256 * 64];
 
   // ---- DMA assignment: wave w fills rows [32w, 32w+32) of both tiles, 8 rows
   // per instruction; lane p writes LDS bytes [16p, 16p+16) of the
@@ -230,13 +351,15 @@ __global__ __launch_bounds__(512) void tiled256_kernel(const uint16_t *__restric
   const uint32_t baseA = uint32_t((wr * 128 + (lane & 31)) * 128);
   const uint32_t baseB = uint32_t((wc * 64 + (lane & 31)) * 128);
 
-  f32x16 acc[4][2];
+  constexpr int FA = 4, FB = 2;  // 128 weight rows x 64 tokens per wavefront
+  f32x16 acc[FA][FB];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < FA; ++f)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < FB; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[f][t][i] = 0.f;
+  bf16x8 fa[2][FA], fb[2][FB];
 
   const int nk = K / 64 / ksplit;  // k-blocks of this part (an even count)
   const int kb0 = tl.ks * nk;
@@ -253,76 +376,14 @@ __global__ __launch_bounds__(512) void tiled256_kernel(const uint16_t *__restric
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
       dma16(xsrc[i] + k0, (lds_void *)(SX + (dma_row + i * 8) * 64));                      \
   }
-  // both fragment sets double-buffered: the next kk's six reads are issued
-  // ahead of the current kk's eight MFMAs
-#define COMPUTE(SW, SX)                                                                    \
-  {                                                                                        \
-    const char *pa = reinterpret_cast<const char *>(SW) + baseA;                           \
-    const char *pb = reinterpret_cast<const char *>(SX) + baseB;                           \
-    bf16x8 fa[2][4], fb[2][2];                                                             \
-    _Pragma("unroll") for (int f = 0; f < 4; ++f)                                          \
-      fa[0][f] = *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[0]);               \
-    _Pragma("unroll") for (int t = 0; t < 2; ++t)                                          \
-      fb[0][t] = *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[0]);               \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                     \
-      const int cur = kk & 1;                                                              \
-      if (kk + 1 < 4) {                                                                    \
-        _Pragma("unroll") for (int f = 0; f < 4; ++f) fa[cur ^ 1][f] =                     \
-            *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[kk + 1]);               \
-        _Pragma("unroll") for (int t = 0; t < 2; ++t) fb[cur ^ 1][t] =                     \
-            *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[kk + 1]);               \
-      }                                                                                    \
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);                                   \
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);                                   \
-      _Pragma("unroll") for (int t = 0; t < 2; ++t)                                        \
-        _Pragma("unroll") for (int f = 0; f < 4; ++f)                                      \
-          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][f], fb[cur][t],      \
-                                                              acc[f][t], 0, 0, 0);         \
-      __builtin_amdgcn_sched_barrier(0);                                                   \
-    }                                                                                      \
-  }
-  // k-block KB: weights in slot KB % 3, tokens in slot KB % 2; the copies
-  // issued go to the slots the previous k-block has just released. Separate
-  // LDS arrays per slot (not one indexed array) let the compiler see that the
-  // copies in flight do not touch the slots being read.
-#define STEP(KB, WS, XS, XN, WN)                                                           \
-  DMAX(sX##XN, (KB) + 1)                                                                   \
-  DMAW(sW##WN, (KB) + 2)                                                                   \
-  COMPUTE(sW##WS, sX##XS)                                                                  \
-  __builtin_amdgcn_s_waitcnt(kWaitVm4);                                                    \
-  TILED_BARRIER()
-
-  DMAW(sW0, 0)
-  DMAX(sX0, 0)
-  DMAW(sW1, 1)
-  __builtin_amdgcn_s_waitcnt(kWaitVm4);
-  TILED_BARRIER()
-  int kt = 0;
-  for (; kt + 6 <= nk; kt += 6) {  // unrolled by 6 so that every slot index is static
-    STEP(kt + 0, 0, 0, 1, 2)
-    STEP(kt + 1, 1, 1, 0, 0)
-    STEP(kt + 2, 2, 0, 1, 1)
-    STEP(kt + 3, 0, 1, 0, 2)
-    STEP(kt + 4, 1, 0, 1, 0)
-    STEP(kt + 5, 2, 1, 0, 1)
-  }
-  if (kt < nk) {  // nk is even: 2 or 4 k-blocks remain
-    STEP(kt + 0, 0, 0, 1, 2)
-    STEP(kt + 1, 1, 1, 0, 0)
-    kt += 2;
-  }
-  if (kt < nk) {
-    STEP(kt + 0, 2, 0, 1, 1)
-    STEP(kt + 1, 0, 1, 0, 2)
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no copy in flight past the main loop
-#undef STEP
+  // 4 weight + 4 token copies per wavefront and k-block; the prologue waits for
+  // k-block 0 with the weights of 1 and 2 and the tokens of 1 in flight
+  constexpr int kStepWait = wait_vm_lgkm0(4);
+  TL_KLOOP(wait_vm(12))
 #undef DMAW
 #undef DMAX
-#undef COMPUTE
 
-  store_2x4<GATEUP, BT>(acc, tl, lane, wr, wc, N, part_stride, out);
+  store_128rows<GATEUP, FB>(acc, tl, lane, wr, wc * 64, N, part_stride, out);
 }
 
 // Small batches (an expert holds a few dozen rows): the weight tiles are read
@@ -339,16 +400,14 @@ __global__ __launch_bounds__(512) void tiled256_kernel(const uint16_t *__restric
 // kernel, whose weight tiles are shared by several token tiles, measured no
 // better with it). The kernels below own the LDS (separate arrays per slot, so that the compiler
 // sees the copies in flight cannot alias the slot being read) and run this body.
-template <bool GATEUP, int BT>
+template <bool GATEUP, int BT, bool THREE_STAGE>
 __device__ __forceinline__ void small_body(
-    const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
-    const uint16_t *__restrict__ Wa, const uint16_t *__restrict__ Wb, void *__restrict__ out,
-    int N, int K, int ksplit, int64_t part_stride, const int32_t *__restrict__ rowmap,
-    uint16_t *sW0, uint16_t *sW1, uint16_t *sW2, uint16_t *sX0, uint16_t *sX1) {
+    const Tile &tl, const uint16_t *__restrict__ X, const uint16_t *__restrict__ Wa,
+    const uint16_t *__restrict__ Wb, void *__restrict__ out, int N, int K, int ksplit,
+    int64_t part_stride, const int32_t *__restrict__ rowmap, uint16_t *sW0, uint16_t *sW1,
+    uint16_t *sW2, uint16_t *sX0, uint16_t *sX1) {
   constexpr int NT = BT / 64;  // 32-token accumulator columns per wavefront
   constexpr int XI = BT / 64;  // token-row DMA instructions per wavefront
-  Tile tl;
-  if (!find_tile<BT, GATEUP ? 128 : 256>(offsets, E, N, ksplit, tl)) return;
   const int e = tl.e, row0 = tl.row0, ne = tl.ne, m0 = tl.m0, c0 = tl.c0, ks = tl.ks;
 
   const int tid = threadIdx.x;
@@ -398,13 +457,15 @@ __device__ __forceinline__ void small_body(
   const uint32_t baseA = uint32_t((wr * 64 + (lane & 31)) * 128);
   const uint32_t baseB = uint32_t((wc * (BT / 2) + (lane & 31)) * 128);
 
-  f32x16 acc[2][NT];
+  constexpr int FA = 2, FB = NT;  // 64 weight rows x BT/2 tokens per wavefront
+  f32x16 acc[FA][FB];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < FA; ++f)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < FB; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[f][t][i] = 0.f;
+  bf16x8 fa[2][FA], fb[2][FB];
 
   const int nk = K / 64 / ksplit;  // k-blocks of this part (an even count)
   const int kb0 = ks * nk;
@@ -413,7 +474,7 @@ __device__ __forceinline__ void small_body(
   {                                                                                        \
     const uint32_t k0 = uint32_t((kb0 + min(KB, nk - 1)) * 64);                            \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
-      dma16_nt(wmat + wofs[i] + k0, (lds_void *)(SW + (dma_row + i * 8) * 64));              \
+      dma16_nt(wmat + wofs[i] + k0, (lds_void *)(SW + (dma_row + i * 8) * 64));            \
   }
 #define DMAX(SX, KB)                                                                       \
   {                                                                                        \
@@ -421,35 +482,15 @@ __device__ __forceinline__ void small_body(
     _Pragma("unroll") for (int i = 0; i < XI; ++i)                                         \
       dma16(xsrc[i] + k0, (lds_void *)(SX + (dma_xrow + i * 8) * 64));                    \
   }
-#define COMPUTE(SW, SX)                                                                    \
-  {                                                                                        \
-    const char *pa = reinterpret_cast<const char *>(SW) + baseA;                           \
-    const char *pb = reinterpret_cast<const char *>(SX) + baseB;                           \
-    bf16x8 fa[2][2], fb[2][NT];                                                            \
-    _Pragma("unroll") for (int f = 0; f < 2; ++f)                                          \
-      fa[0][f] = *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[0]);               \
-    _Pragma("unroll") for (int t = 0; t < NT; ++t)                                         \
-      fb[0][t] = *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[0]);               \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                     \
-      const int cur = kk & 1;                                                              \
-      if (kk + 1 < 4) {                                                                    \
-        _Pragma("unroll") for (int f = 0; f < 2; ++f) fa[cur ^ 1][f] =                     \
-            *reinterpret_cast<const bf16x8 *>(pa + f * 4096 + offk[kk + 1]);               \
-        _Pragma("unroll") for (int t = 0; t < NT; ++t) fb[cur ^ 1][t] =                    \
-            *reinterpret_cast<const bf16x8 *>(pb + t * 4096 + offk[kk + 1]);               \
-      }                                                                                    \
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 + NT, 1);                              \
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NT, 1);                              \
-      _Pragma("unroll") for (int t = 0; t < NT; ++t)                                       \
-        _Pragma("unroll") for (int f = 0; f < 2; ++f)                                      \
-          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][f], fb[cur][t],      \
-                                                              acc[f][t], 0, 0, 0);         \
-      __builtin_amdgcn_sched_barrier(0);                                                   \
-    }                                                                                      \
-  }
-
-  if constexpr (BT == 64) {
+  if constexpr (!THREE_STAGE) {
+    // two stages of both: the next k-block's copies are issued, the current one
+    // is multiplied, then a wait for all copies and a barrier
+#define TL_BLOCK(SW, SX)                                                                   \
+  TL_READ(SW, SX, 0, 0)                                                                    \
+  TL_KSTEP(SW, SX, 1, 1, 0)                                                                \
+  TL_KSTEP(SW, SX, 2, 0, 1)                                                                \
+  TL_KSTEP(SW, SX, 3, 1, 0)                                                                \
+  TL_KLAST(1)
     DMAW(sW0, 0)
     DMAX(sX0, 0)
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -457,52 +498,24 @@ __device__ __forceinline__ void small_body(
     for (int kt = 0; kt < nk; kt += 2) {
       DMAW(sW1, kt + 1)
       DMAX(sX1, kt + 1)
-      COMPUTE(sW0, sX0)
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      TL_BLOCK(sW0, sX0)
+      __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
       __syncthreads();
       DMAW(sW0, kt + 2)
       DMAX(sX0, kt + 2)
-      COMPUTE(sW1, sX1)
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      TL_BLOCK(sW1, sX1)
+      __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
       __syncthreads();
     }
+#undef TL_BLOCK
   } else {
-    // as tiled256_kernel: tokens one k-block ahead, weights two
-#define STEP(KB, WS, XS, XN, WN)                                                           \
-  DMAX(sX##XN, (KB) + 1)                                                                   \
-  DMAW(sW##WN, (KB) + 2)                                                                   \
-  COMPUTE(sW##WS, sX##XS)                                                                  \
-  __builtin_amdgcn_s_waitcnt(kWaitVm4);                                                    \
-  TILED_BARRIER()
-    DMAW(sW0, 0)
-    DMAX(sX0, 0)
-    DMAW(sW1, 1)
-    __builtin_amdgcn_s_waitcnt(kWaitVm4);
-    TILED_BARRIER()
-    int kt = 0;
-    for (; kt + 6 <= nk; kt += 6) {
-      STEP(kt + 0, 0, 0, 1, 2)
-      STEP(kt + 1, 1, 1, 0, 0)
-      STEP(kt + 2, 2, 0, 1, 1)
-      STEP(kt + 3, 0, 1, 0, 2)
-      STEP(kt + 4, 1, 0, 1, 0)
-      STEP(kt + 5, 2, 1, 0, 1)
-    }
-    if (kt < nk) {
-      STEP(kt + 0, 0, 0, 1, 2)
-      STEP(kt + 1, 1, 1, 0, 0)
-      kt += 2;
-    }
-    if (kt < nk) {
-      STEP(kt + 0, 2, 0, 1, 1)
-      STEP(kt + 1, 0, 1, 0, 2)
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no copy in flight past the main loop
-#undef STEP
+    // as the 256-token tile (4 weight and XI token copies per wavefront and
+    // k-block)
+    constexpr int kStepWait = wait_vm_lgkm0(4);
+    TL_KLOOP(wait_vm(8 + XI))
   }
 #undef DMAW
 #undef DMAX
-#undef COMPUTE
 
   // ---- epilogue (fragment layout as in tiled_kernel)
   const int ih = 4 * (lane >> 5);
@@ -549,8 +562,10 @@ __global__ __launch_bounds__(512) void tiled64_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX0[64 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX1[64 * 64];
-  small_body<GATEUP, 64>(X, offsets, E, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0,
-                         sW1, nullptr, sX0, sX1);
+  Tile tl;
+  if (!find_tile<64, GATEUP ? 128 : 256>(offsets, E, N, ksplit, tl)) return;
+  small_body<GATEUP, 64, false>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1,
+                                nullptr, sX0, sX1);
 }
 
 template <bool GATEUP>
@@ -563,8 +578,40 @@ __global__ __launch_bounds__(512) void tiled128_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t sW2[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX0[128 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX1[128 * 64];
-  small_body<GATEUP, 128>(X, offsets, E, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0,
-                          sW1, sW2, sX0, sX1);
+  Tile tl;
+  if (!find_tile<128, GATEUP ? 128 : 256>(offsets, E, N, ksplit, tl)) return;
+  small_body<GATEUP, 128, true>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1,
+                                sW2, sX0, sX1);
+}
+
+// Experts of more than a few hundred rows: 256-token tiles (body256), each
+// expert's last, partly filled tile narrowed to 64 or 128 tokens (small_body
+// with the three-stage pipeline of the 256-token tile); the width is found per
+// workgroup from offsets, so one launch needs no host-side knowledge of the
+// routing. The three bodies share this kernel's LDS (160 KiB). min_tail: the
+// narrowest tail tile (64; 256 keeps every tile 256 tokens wide).
+template <bool GATEUP>
+__global__ __launch_bounds__(512) void tiled256_kernel(
+    const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
+    const uint16_t *__restrict__ Wa, const uint16_t *__restrict__ Wb, void *__restrict__ out,
+    int N, int K, int ksplit, int64_t part_stride, const int32_t *__restrict__ rowmap,
+    int min_tail) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sW0[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW2[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX0[256 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX1[256 * 64];
+  Tile tl;
+  if (!find_tile_mixed<GATEUP ? 128 : 256>(offsets, E, N, ksplit, min_tail, tl)) return;
+  if (tl.bt == 256)
+    body256<GATEUP>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1, sW2, sX0,
+                    sX1);
+  else if (tl.bt == 128)
+    small_body<GATEUP, 128, true>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1,
+                                  sW2, sX0, sX1);
+  else
+    small_body<GATEUP, 64, true>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1,
+                                 sW2, sX0, sX1);
 }
 
 // Upper bound of the tile count for any split of S rows over E experts.
@@ -590,7 +637,7 @@ void launch_bt(int bt, const void *x, const int32_t *rowmap, const int32_t *offs
                        out, N, K, ksplit, part_stride, rowmap);
   else
     hipLaunchKernelGGL((tiled256_kernel<GATEUP>), grid, dim3(512), 0, s, xp, offsets, E, ap, bp,
-                       out, N, K, ksplit, part_stride, rowmap);
+                       out, N, K, ksplit, part_stride, rowmap, 64);
 }
 
 }  // namespace
