@@ -61,6 +61,10 @@ def parse():
                     help="comma-separated batch sizes T: time moe_forward on both expert paths "
                          "at each T with the workload's d, h and distributions (prints one JSON "
                          "line with the table instead of the bench line)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor GEMM library (torch.matmul, bf16) on the expert "
+                         "projections' shapes of the workload, dense over all S = T*K rows and on "
+                         "one expert's even share: the reference point for the tiled kernels")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (steps "
                          "times): the reference kernel for scaling HBM byte counters")
@@ -82,6 +86,40 @@ def copy_probe(mib: int, steps: int):
     print(json.dumps({"copy_probe_mib": mib, "read_bytes": n * 4, "write_bytes": n * 4,
                       "ms_per_copy": round(dt * 1e3, 4),
                       "GBps_read_plus_write": round(2 * n * 4 / dt / 1e9, 1)}), flush=True)
+    return 0
+
+
+def vendor_gemm(args):
+    """torch.matmul (the vendor GEMM library) on the workload's projection shapes:
+    gate-up [rows, d] x [d, 2h] and down [rows, h] x [h, d], for rows = S (the whole
+    routed batch as one dense GEMM) and rows = S / E (one expert's even share)."""
+    import torch
+
+    import moe_inputs as mi
+
+    cfg = mi.CONFIGS[args.workload]
+    S, d, h, E = cfg.S, cfg.d, cfg.h, cfg.E
+    g = torch.Generator(device="cuda").manual_seed(0)
+    rows_out = []
+    for name, M, K, N in (("gate_up_dense", S, d, 2 * h), ("gate_up_one_expert", S // E, d, 2 * h),
+                          ("down_dense", S, h, d), ("down_one_expert", S // E, h, d)):
+        a = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        b = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        for _ in range(3):
+            a @ b.t()
+        torch.cuda.synchronize()
+        n = max(5, min(args.steps, 50))
+        t0 = time.perf_counter()
+        for _ in range(n):
+            a @ b.t()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / n
+        tf = 2.0 * M * N * K / (ms / 1e3) / 1e12
+        rows_out.append({"gemm": name, "M": M, "K": K, "N": N, "ms": round(ms, 4),
+                         "TFLOP/s": round(tf, 1), "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        print(f"# {name}: {M} x {K} x {N}: {ms:.3f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del a, b
+    print(json.dumps({"vendor_gemm": cfg.name, "rows": rows_out}), flush=True)
     return 0
 
 
@@ -178,6 +216,8 @@ def main():
         return copy_probe(args.copy_probe_mib, max(1, args.steps))
     if args.sweep:
         return sweep(args)
+    if args.vendor_gemm:
+        return vendor_gemm(args)
 
     import torch
 
@@ -359,13 +399,15 @@ def measure(workload: str, args, cpu_seconds: float) -> dict:
     traffic = None
     traffic_detail = None
     if traffic_rec:
-        # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, each scaled by
-        # what the same counter reads for a plain 1 GiB device copy
-        traffic = traffic_rec["fetch_bytes_per_launch"] + traffic_rec["write_bytes_per_launch"]
-        traffic_detail = {"fetch_bytes": traffic_rec["fetch_bytes_per_launch"],
+        # HBM bytes per launch from rocprofv3: reads from the L2's sized read requests
+        # (exact for a 1 GiB device copy), writes from WRITE_SIZE scaled by what it reads
+        # for that copy
+        traffic = traffic_rec["read_bytes_per_launch"] + traffic_rec["write_bytes_per_launch"]
+        traffic_detail = {"read_bytes": traffic_rec["read_bytes_per_launch"],
                           "write_bytes": traffic_rec["write_bytes_per_launch"],
-                          "fetch_scale": traffic_rec["fetch_scale"],
+                          "fetch_size_kib_raw": traffic_rec["fetch_size_kib_per_dispatch_raw"],
                           "write_scale": traffic_rec["write_scale"],
+                          "over_algorithmic": traffic_rec["traffic_over_algorithmic"],
                           "source": f"profiles/traffic_{kernel}_{cfg.name}.json"}
     if path == "stream":
         achieved = gu_bytes / (gu_ms / 1e3) / 1e9

@@ -176,50 +176,12 @@ __device__ __forceinline__ void dma16_nt(const uint16_t *g, lds_void *l) {
 }
 
 // The tile of this workgroup: expert e (rows row0 .. row0 + ne - 1), token
-// block m0 of bt tokens, output column c0 and, with ksplit > 1 (down only), the
-// part ks of the sum over K. False when the workgroup has no tile.
+// block m0, output column c0 and, with ksplit > 1 (down only), the part ks of
+// the sum over K. False when the workgroup has no tile.
 struct Tile {
-  int e, row0, ne, m0, c0, ks, bt;
+  int e, row0, ne, m0, c0, ks;
 };
 
-// Width of the last token tile of an expert whose rows leave `rem` (1-255) past
-// its full 256-token tiles: the narrowest of 64, 128, 256 that holds them.
-__device__ __forceinline__ int tail_width(int rem) { return rem <= 64 ? 64 : rem <= 128 ? 128 : 256; }
-
-// Tiles of 256 tokens, except that each expert's last, partly filled token tile
-// is only as wide as tail_width(rows % 256): the matrix work spent on rows past
-// an expert's end shrinks from up to 255 rows to at most 63 (at the 8x7B prefill
-// shape, 33 instead of 36 full tiles' worth). Order and XCD mapping as
-// find_tile.
-template <int kCols>
-__device__ __forceinline__ bool find_tile_mixed(const int32_t *__restrict__ offsets, int E, int N,
-                                                int ksplit, int min_tail, Tile &tl) {
-  const int ct = (N + kCols - 1) / kCols;
-  int total = 0;
-  for (int q = 0; q < E; ++q) total += ct * ((offsets[q + 1] - offsets[q] + 255) / 256);
-  const int g8 = (total * ksplit + kXCD - 1) / kXCD;
-  const int b = blockIdx.x;
-  if (b >= g8 * kXCD) return false;
-  int L = (b % kXCD) * g8 + b / kXCD;
-  if (L >= total * ksplit) return false;
-  tl.ks = L / total;
-  L -= tl.ks * total;
-  int e = 0, row0 = 0, ne = 0, mtiles = 0;
-  for (; e < E; ++e) {
-    row0 = offsets[e];
-    ne = offsets[e + 1] - row0;
-    mtiles = (ne + 255) / 256;
-    if (L < ct * mtiles) break;
-    L -= ct * mtiles;
-  }
-  tl.e = e;
-  tl.row0 = row0;
-  tl.ne = ne;
-  tl.m0 = (L % mtiles) * 256;
-  tl.c0 = (L / mtiles) * kCols;
-  tl.bt = ne - tl.m0 >= 256 ? 256 : max(tail_width(ne - tl.m0), min_tail);
-  return true;
-}
 template <int BT, int kCols>
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int N,
                                           int ksplit, Tile &tl) {
@@ -246,7 +208,6 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
   tl.ne = ne;
   tl.m0 = (L % mtiles) * BT;
   tl.c0 = (L / mtiles) * kCols;
-  tl.bt = BT;
   return true;
 }
 
@@ -584,34 +545,30 @@ __global__ __launch_bounds__(512) void tiled128_kernel(
                                 sW2, sX0, sX1);
 }
 
-// Experts of more than a few hundred rows: 256-token tiles (body256), each
-// expert's last, partly filled tile narrowed to 64 or 128 tokens (small_body
-// with the three-stage pipeline of the 256-token tile); the width is found per
-// workgroup from offsets, so one launch needs no host-side knowledge of the
-// routing. The three bodies share this kernel's LDS (160 KiB). min_tail: the
-// narrowest tail tile (64; 256 keeps every tile 256 tokens wide).
+// Experts of more than a few hundred rows: 256-token tiles (body256).
+// Narrowing each expert's last, partly filled tile to 64 or 128 tokens (33
+// instead of 36 full tiles' worth of matrix work at the 8x7B prefill shape)
+// was measured on MI355X, in one process, interleaved: gate-up 1.79 vs 1.81 ms
+// and down 0.95 vs 0.97 ms on the mean, no gain on the best runs, and twice
+// the HBM reads (3.1 -> 5.9 GB per gate-up launch): a narrow tail has a quarter
+// of a full tile's matrix work, runs ahead of its expert's full tiles of the
+// same column block through the k-loop and fetches the shared weight slices
+// first, and the full tiles then find them evicted from L2. Running all tails
+// after the full tiles cut that to 4.7 GB and was slower. Every tile is 256
+// tokens wide.
 template <bool GATEUP>
 __global__ __launch_bounds__(512) void tiled256_kernel(
     const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
     const uint16_t *__restrict__ Wa, const uint16_t *__restrict__ Wb, void *__restrict__ out,
-    int N, int K, int ksplit, int64_t part_stride, const int32_t *__restrict__ rowmap,
-    int min_tail) {
+    int N, int K, int ksplit, int64_t part_stride, const int32_t *__restrict__ rowmap) {
   __shared__ __attribute__((aligned(1024))) uint16_t sW0[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sW1[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sW2[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX0[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX1[256 * 64];
   Tile tl;
-  if (!find_tile_mixed<GATEUP ? 128 : 256>(offsets, E, N, ksplit, min_tail, tl)) return;
-  if (tl.bt == 256)
-    body256<GATEUP>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1, sW2, sX0,
-                    sX1);
-  else if (tl.bt == 128)
-    small_body<GATEUP, 128, true>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1,
-                                  sW2, sX0, sX1);
-  else
-    small_body<GATEUP, 64, true>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1,
-                                 sW2, sX0, sX1);
+  if (!find_tile<256, GATEUP ? 128 : 256>(offsets, E, N, ksplit, tl)) return;
+  body256<GATEUP>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1, sW2, sX0, sX1);
 }
 
 // Upper bound of the tile count for any split of S rows over E experts.
@@ -637,7 +594,7 @@ void launch_bt(int bt, const void *x, const int32_t *rowmap, const int32_t *offs
                        out, N, K, ksplit, part_stride, rowmap);
   else
     hipLaunchKernelGGL((tiled256_kernel<GATEUP>), grid, dim3(512), 0, s, xp, offsets, E, ap, bp,
-                       out, N, K, ksplit, part_stride, rowmap, 64);
+                       out, N, K, ksplit, part_stride, rowmap);
 }
 
 }  // namespace
