@@ -10,17 +10,19 @@
 // Tile: 256 weight rows (MFMA M side) x BT tokens (MFMA N side) x 64 k, BT = 64,
 // 128 or 256 by the rows an expert holds (chosen on the host).
 //  * BT = 256: 8 wavefronts (2 per SIMD) in a 2 x 4 grid; each owns 128 weight
-//    rows x 64 tokens as 4 x 2 accumulators of v_mfma_f32_32x32x16_bf16. Two
+//    rows x 64 tokens as 8 x 4 accumulators of v_mfma_f32_16x16x32_bf16. Two
 //    wavefronts per SIMD keep the matrix pipe fed while the other waits on LDS
 //    or a barrier. The LDS holds three weight stages, so weight tiles are
 //    fetched two k-blocks ahead of their use.
+//  * BT = 64, 128: 8 wavefronts in a 4 x 2 grid of v_mfma_f32_32x32x16_bf16
+//    tiles (the 32 x 32 shape needs fewer fragment registers per token).
 //  * Global memory goes straight to LDS (global_load_lds_dwordx4: a wavefront
 //    instruction fills one contiguous kilobyte, lane L the bytes [16L, 16L+16));
 //    one barrier per k-block.
-//  * LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by
-//    (r ^ r >> 3) & 7 of the row's position in its 32-row group, so both the
-//    DMA writes and the fragment reads of 8 or 16 consecutive rows hit distinct
-//    banks (measured: zero bank conflicts).
+//  * LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by swz() of
+//    the row's position in its 32-row group, so that the fragment reads of both
+//    MFMA shapes hit distinct banks in every pass of the LDS (measured: zero
+//    bank conflicts); the DMA writes are contiguous kilobytes.
 //  * Gate-up: the 256 weight rows are W1 and W3 rows of the same 128 output
 //    columns, interleaved so that every wavefront holds g and u of the same
 //    columns and applies silu(g) * u in registers; the result is rounded once to
@@ -35,8 +37,8 @@
 //    its own writing float32 partial sums that the combine step adds in a fixed
 //    order, so that the last round of tiles fills the GPU.
 //  * Every variant sums each output over k in the same order (64-wide k-blocks
-//    in order, 16-wide MFMA steps within), so the tile width changes no bit of
-//    the result.
+//    in order, 16-wide halves of the MFMA steps within), so neither the tile
+//    width nor the MFMA shape changes a bit of the result.
 #include "kernels.h"
 
 namespace moe {
@@ -162,7 +164,19 @@ constexpr int wait_vm_lgkm0(int n) { return ((n >> 4) << 14) | 0x0070 | (n & 15)
   __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
 
 // Physical 16-byte chunk = logical chunk ^ swz(row); depends on row & 31 only.
-__device__ __forceinline__ int swz(int r) { return ((r & 31) ^ ((r & 31) >> 3)) & 7; }
+// A wavefront's ds_read_b128 is served in four passes of 16 lanes; lane 0 shares
+// its pass with lanes 1-3, 12-15, 20-23 and 24-27 (the 4-lane groups whose index
+// bits XOR to the same parity within each half-wavefront), 64 banks of 4 bytes
+// (measured on MI355X with single-wavefront address patterns). For both fragment
+// shapes below (32 rows x 2 chunks per 32 x 32 operand, 16 rows x 4 chunks per
+// 16 x 16 operand) this swizzle puts every pass on 16 distinct 4-bank groups;
+// (r ^ r >> 3) & 7, which is conflict-free for the 32-row reads, costs 1.5x on the
+// 16-row ones.
+__host__ __device__ constexpr int swz(int r) { return (r & 7) ^ ((r >> 4) & 1); }
+// the odd 16-row half of a 32-row group has the swizzle of the even half XOR this
+// (as a byte offset)
+constexpr int kOddXor = (swz(16) ^ swz(0)) * 16;
+static_assert(((swz(16) ^ swz(0)) == (swz(31) ^ swz(15))), "odd-half swizzle is one XOR");
 
 // One global -> LDS copy of 16 bytes per lane (a plain function: the builtin
 // inside a kernel template can fail the template's host-side instantiation).
@@ -211,56 +225,111 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
   return true;
 }
 
-// Epilogue of a wavefront that owns 128 weight rows (wr) x NT * 32 tokens from
-// token `tok0` of its tile: lane holds token column j = lane & 31 and weight rows
-// i = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4) of each 32x32 fragment; gate-up
-// fragments 0, 1 are g and 2, 3 the u of the same columns.
-template <bool GATEUP, int NT>
-__device__ __forceinline__ void store_128rows(const f32x16 (&acc)[4][NT], const Tile &tl,
-                                              int lane, int wr, int tok0, int N,
-                                              int64_t part_stride, void *__restrict__ out) {
-  const int ih = 4 * (lane >> 5);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int tok = tl.m0 + tok0 + t * 32 + (lane & 31);
-    if (tok >= tl.ne) continue;
-    const size_t orow = size_t(tl.row0 + tok) * N + size_t(tl.ks) * size_t(part_stride);
-    if constexpr (GATEUP) {
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = tl.c0 + wr * 64 + f * 32 + 8 * q + ih;
-          if (col >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) v[s] = silu(acc[f][t][4 * q + s]) * acc[f + 2][t][4 * q + s];
-          uint2 pk;
-          pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-          pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + orow + col) = pk;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = tl.c0 + wr * 128 + f * 32 + 8 * q + ih;
-          if (col >= N) continue;
-          *reinterpret_cast<float4 *>(static_cast<float *>(out) + orow + col) =
-              make_float4(acc[f][t][4 * q], acc[f][t][4 * q + 1], acc[f][t][4 * q + 2],
-                          acc[f][t][4 * q + 3]);
-        }
-      }
-    }
+// ---- BT = 256: the 16 x 16 x 32 body ---------------------------------------------
+// 8 wavefronts (2 per SIMD) in a 2 x 4 grid; each owns 128 weight rows x 64 tokens
+// as 8 x 4 accumulators of v_mfma_f32_16x16x32_bf16 (A: lane holds weight row
+// lane & 15 and k 8 (lane >> 4) + 0..7 of a 32-wide k-step; B the same for a token;
+// D: token lane & 15, weight rows 4 (lane >> 4) + 0..3). A 64-wide k-block is two
+// 32-wide k-steps. On MI355X this shape runs the same tile 4-6% faster than the
+// 32 x 32 x 16 one (the clock holds about 0.15 GHz higher at the same matrix work)
+// and gives the same sums to the bit: both add the products of each 16-wide half of
+// a 32-wide k-step into the accumulator in the same order.
+//
+// Fragment f (weight rows 16 f .. 16 f + 15 of the wavefront's block, or tokens
+// 16 t ..), k-step kk: logical chunk 4 kk + (lane >> 4) of row 16 f + (lane & 15)
+// sits at physical chunk (lane >> 4) ^ swz(lane & 15) ^ 4 kk ^ (f & 1) kOddXor / 16,
+// so every read address is lane_base ^ (64 kk | (f & 1) kOddXor) + 2048 f. The empty
+// asm hands each k-step a fresh copy of the lane base, so that the compiler does not
+// keep one address register per slot, k-step and parity live across the loop.
+#define M16_READ_B(SX, KK, BUF)                                                            \
+  {                                                                                        \
+    uint32_t lb_ = laneB;                                                                  \
+    asm volatile("" : "+v"(lb_));                                                          \
+    const char *p0_ = reinterpret_cast<const char *>(SX) + (lb_ ^ (64 * (KK)));            \
+    const char *p1_ = reinterpret_cast<const char *>(SX) + (lb_ ^ (64 * (KK) + kOddXor));  \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) fb[BUF][t] =                             \
+        *reinterpret_cast<const bf16x8 *>(((t & 1) ? p1_ : p0_) + t * 2048);               \
   }
-}
+#define M16_READ_A(SW, KK, BUF, H)                                                         \
+  {                                                                                        \
+    uint32_t la_ = laneA;                                                                  \
+    asm volatile("" : "+v"(la_));                                                          \
+    const char *p0_ = reinterpret_cast<const char *>(SW) + (la_ ^ (64 * (KK)));            \
+    const char *p1_ = reinterpret_cast<const char *>(SW) + (la_ ^ (64 * (KK) + kOddXor));  \
+    _Pragma("unroll") for (int f = 4 * (H); f < 4 * (H) + 4; ++f) fa[BUF][f] =             \
+        *reinterpret_cast<const bf16x8 *>(((f & 1) ? p1_ : p0_) + f * 2048);               \
+  }
+#define M16_MFMA(BUF, H)                                                                   \
+  _Pragma("unroll") for (int f = 4 * (H); f < 4 * (H) + 4; ++f)                           \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                          \
+      acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[BUF][f], fb[BUF][t], acc[f][t], \
+                                                          0, 0, 0);
+// Multiply the fragments in BUF while k-step KKN of (SW, SX) is read into BUFN, in
+// two halves so that only half of the weight fragments are double-buffered (the
+// registers hold 128 accumulators): the token fragments and weight fragments 0-3
+// are read after the first MFMA of the k-step, weight fragments 4-7 after the first
+// MFMA of its second half, when fragments 0-3 of this k-step have been consumed.
+#define M16_KSTEP(SW, SX, KKN, BUFN, BUF)                                                  \
+  M16_READ_B(SX, KKN, BUFN)                                                                \
+  M16_READ_A(SW, KKN, BUFN, 0)                                                             \
+  M16_MFMA(BUF, 0)                                                                         \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 15, 0);                                      \
+  __builtin_amdgcn_sched_barrier(0);                                                       \
+  M16_READ_A(SW, KKN, BUFN, 1)                                                             \
+  M16_MFMA(BUF, 1)                                                                         \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 15, 0);                                      \
+  __builtin_amdgcn_sched_barrier(0);
+// One k-block with the pipeline of TL_STEP: k-step 0 is multiplied while k-step 1
+// is read, the wait and the barrier, the copies of KB + 2 (tokens) and KB + 3
+// (weights), then k-step 1 is multiplied while k-step 0 of KB + 1 is read.
+#define M16_STEP(KB, WS, XS, WN, XN)                                                       \
+  M16_KSTEP(sW##WS, sX##XS, 1, 1, 0)                                                       \
+  __builtin_amdgcn_s_waitcnt(kStepWait);                                                   \
+  TILED_BARRIER()                                                                          \
+  DMAX(sX##XS, (KB) + 2)                                                                   \
+  DMAW(sW##WS, (KB) + 3)                                                                   \
+  M16_KSTEP(sW##WN, sX##XN, 0, 0, 1)
+#define M16_KLOOP(PROLOGUE_WAIT)                                                           \
+  DMAW(sW0, 0)                                                                             \
+  DMAX(sX0, 0)                                                                             \
+  DMAW(sW1, 1)                                                                             \
+  DMAX(sX1, 1)                                                                             \
+  DMAW(sW2, 2)                                                                             \
+  __builtin_amdgcn_s_waitcnt(PROLOGUE_WAIT); /* k-block 0 has landed */                    \
+  TILED_BARRIER()                                                                          \
+  M16_READ_B(sX0, 0, 0)                                                                    \
+  M16_READ_A(sW0, 0, 0, 0)                                                                 \
+  M16_READ_A(sW0, 0, 0, 1)                                                                 \
+  {                                                                                        \
+    int kt = 0;                                                                            \
+    for (; kt + 6 <= nk; kt += 6) {                                                        \
+      M16_STEP(kt + 0, 0, 0, 1, 1)                                                         \
+      M16_STEP(kt + 1, 1, 1, 2, 0)                                                         \
+      M16_STEP(kt + 2, 2, 0, 0, 1)                                                         \
+      M16_STEP(kt + 3, 0, 1, 1, 0)                                                         \
+      M16_STEP(kt + 4, 1, 0, 2, 1)                                                         \
+      M16_STEP(kt + 5, 2, 1, 0, 0)                                                         \
+    }                                                                                      \
+    if (kt < nk) { /* 2 or 4 k-blocks remain */                                            \
+      M16_STEP(kt + 0, 0, 0, 1, 1)                                                         \
+      M16_STEP(kt + 1, 1, 1, 2, 0)                                                         \
+      kt += 2;                                                                             \
+    }                                                                                      \
+    if (kt < nk) {                                                                         \
+      M16_STEP(kt + 0, 2, 0, 0, 1)                                                         \
+      M16_STEP(kt + 1, 0, 1, 1, 0)                                                         \
+    }                                                                                      \
+  }                                                                                        \
+  /* no copy or read in flight past the loop (the last step read ahead) */                 \
+  __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
 
-// BT = 256: three weight stages and two token stages (160 KiB of LDS), the
-// pipeline of TL_KLOOP. The weight tile of the first token block to reach a
-// k-block is an HBM miss; about two k-blocks of lead hide more of that latency
-// than one (measured 4-9% faster than two stages of both).
+// Three weight stages and two token stages (160 KiB of LDS). The weight tile of the
+// first token block to reach a k-block is an HBM miss; about two k-blocks of lead
+// hide more of that latency than one (measured 4-9% faster than two stages of both).
 template <bool GATEUP>
 __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restrict__ X,
                                         const uint16_t *__restrict__ Wa,
@@ -271,14 +340,16 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
                                         uint16_t *sX1) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 2, wc = wave & 3;
 
   // ---- DMA assignment: wave w fills rows [32w, 32w+32) of both tiles, 8 rows
   // per instruction; lane p writes LDS bytes [16p, 16p+16) of the
   // instruction's kilobyte: row 8i + p/8, physical chunk p%8 = logical chunk ^
   // swz(row). Gate-up weight rows: 64 W1 rows, the W3 rows of the same
-  // columns, the next 64 W1 rows, their W3 rows.
+  // columns, the next 64 W1 rows, their W3 rows. Weight offsets are bytes from
+  // the expert's matrix (h d < 2^31, so they fit 32 bits), so the copies take a
+  // uniform base and a 32-bit per-lane offset.
   const size_t mat_elems = size_t(N) * K;
   const uint16_t *wmat = Wa + size_t(tl.e) * mat_elems;
   if (GATEUP && ((wave >> 1) & 1)) wmat = Wb + size_t(tl.e) * mat_elems;
@@ -293,7 +364,7 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
     int wrow;
     if constexpr (GATEUP) wrow = tl.c0 + ((r >> 7) << 6) + (r & 63);
     else wrow = min(tl.c0 + r, N - 1);
-    wofs[i] = uint32_t(wrow) * uint32_t(K) + c * 8;
+    wofs[i] = (uint32_t(wrow) * uint32_t(K) + c * 8) * 2u;
     if (r > tl.ne - 1 - tl.m0 && K <= kZeroK) {
       xsrc[i] = g_zero_row + c * 8;
     } else {
@@ -303,24 +374,20 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
   }
   const int dma_row = wave * 32;
 
-  // ---- fragment read addresses (bytes): row (lane & 31) of a 32-row group,
-  // logical chunk kk*2 + (lane >> 5)
-  const int g = (lane >> 5) ^ swz(lane & 31);
-  uint32_t offk[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) offk[kk] = uint32_t(((kk * 2) ^ g) * 16);
-  const uint32_t baseA = uint32_t((wr * 128 + (lane & 31)) * 128);
-  const uint32_t baseB = uint32_t((wc * 64 + (lane & 31)) * 128);
+  // ---- fragment read bases (bytes): row lane & 15 of the wavefront's first
+  // weight (token) fragment, physical chunk of logical chunk lane >> 4
+  const uint32_t lchunk = uint32_t(((lane >> 4) ^ swz(lane & 15)) << 4);
+  const uint32_t laneA = uint32_t((wr * 128 + (lane & 15)) * 128) | lchunk;
+  const uint32_t laneB = uint32_t((wc * 64 + (lane & 15)) * 128) | lchunk;
 
-  constexpr int FA = 4, FB = 2;  // 128 weight rows x 64 tokens per wavefront
-  f32x16 acc[FA][FB];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int f = 0; f < FA; ++f)
+  for (int f = 0; f < 8; ++f)
 #pragma unroll
-    for (int t = 0; t < FB; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[f][t][i] = 0.f;
-  bf16x8 fa[2][FA], fb[2][FB];
+      for (int i = 0; i < 4; ++i) acc[f][t][i] = 0.f;
+  bf16x8 fa[2][8], fb[2][4];
 
   const int nk = K / 64 / ksplit;  // k-blocks of this part (an even count)
   const int kb0 = tl.ks * nk;
@@ -329,7 +396,9 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
   {                                                                                        \
     const uint32_t k0 = uint32_t((kb0 + min(KB, nk - 1)) * 64);                            \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
-      dma16(wmat + wofs[i] + k0, (lds_void *)(SW + (dma_row + i * 8) * 64));               \
+      dma16(reinterpret_cast<const uint16_t *>(                                            \
+                reinterpret_cast<const char *>(wmat + k0) + wofs[i]),                       \
+            (lds_void *)(SW + (dma_row + i * 8) * 64));                                      \
   }
 #define DMAX(SX, KB)                                                                       \
   {                                                                                        \
@@ -340,11 +409,42 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
   // 4 weight + 4 token copies per wavefront and k-block; the prologue waits for
   // k-block 0 with the weights of 1 and 2 and the tokens of 1 in flight
   constexpr int kStepWait = wait_vm_lgkm0(4);
-  TL_KLOOP(wait_vm(12))
+  M16_KLOOP(wait_vm(12))
 #undef DMAW
 #undef DMAX
 
-  store_128rows<GATEUP, FB>(acc, tl, lane, wr, wc * 64, N, part_stride, out);
+  // ---- epilogue: lane holds token wc * 64 + 16 t + (lane & 15) and weight rows
+  // 16 f + 4 (lane >> 4) + 0..3 of the wavefront's 128; for gate-up fragments 0-3
+  // are g and 4-7 the u of the same 64 columns
+  const int ih = 4 * (lane >> 4);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int tok = tl.m0 + wc * 64 + t * 16 + (lane & 15);
+    if (tok >= tl.ne) continue;
+    const size_t orow = size_t(tl.row0 + tok) * N + size_t(tl.ks) * size_t(part_stride);
+    if constexpr (GATEUP) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int col = tl.c0 + wr * 64 + f * 16 + ih;
+        if (col >= N) continue;
+        float v[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) v[s] = silu(acc[f][t][s]) * acc[f + 4][t][s];
+        uint2 pk;
+        pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+        pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + orow + col) = pk;
+      }
+    } else {
+#pragma unroll
+      for (int f = 0; f < 8; ++f) {
+        const int col = tl.c0 + wr * 128 + f * 16 + ih;
+        if (col >= N) continue;
+        *reinterpret_cast<float4 *>(static_cast<float *>(out) + orow + col) =
+            make_float4(acc[f][t][0], acc[f][t][1], acc[f][t][2], acc[f][t][3]);
+      }
+    }
+  }
 }
 
 // Small batches (an expert holds a few dozen rows): the weight tiles are read
@@ -373,7 +473,7 @@ __device__ __forceinline__ void small_body(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
 
   // ---- DMA assignment as in tiled_kernel: wave w fills weight rows
@@ -390,7 +490,7 @@ __device__ __forceinline__ void small_body(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int lr = lane >> 3;
-    const int c = (lane & 7) ^ lr ^ i;  // swz of row 8i + lr in its 32-row group
+    const int c = (lane & 7) ^ swz(8 * i + lr);
     int wrow;
     if constexpr (GATEUP) wrow = c0 + (wave >> 1) * 32 + 8 * i + lr;
     else wrow = min(c0 + dma_row + 8 * i + lr, N - 1);
@@ -399,8 +499,7 @@ __device__ __forceinline__ void small_body(
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int lr = lane >> 3;
-    const int q = (dma_xrow / 8 + i) & 3;
-    const int chunk = ((lane & 7) ^ lr ^ q) << 3;
+    const int chunk = ((lane & 7) ^ swz(dma_xrow + 8 * i + lr)) << 3;
     if (dma_xrow + 8 * i + lr > xlim && K <= kZeroK) {
       xsrc[i] = g_zero_row + chunk;  // padding row
     } else {
