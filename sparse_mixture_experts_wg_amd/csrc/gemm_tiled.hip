@@ -283,16 +283,45 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
   __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                       \
   __builtin_amdgcn_sched_group_barrier(0x008, 15, 0);                                      \
   __builtin_amdgcn_sched_barrier(0);
+// The k-step behind a barrier, with the copies into the slots the barrier freed
+// (tokens of KB + 2 from DX, weights of KB + 3 from DW) issued one at a time between
+// groups of three MFMAs instead of as a burst in front of them: the copy stream
+// reaches the memory system evenly, and on MI355X both projections ran 5% faster
+// (bitwise the same sums).
+#define M16_SPREAD4                                                                        \
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+#define M16_KSTEP_COPY(SW, SX, KKN, BUFN, BUF, DX, DW, KB)                                 \
+  M16_READ_B(SX, KKN, BUFN)                                                                \
+  M16_READ_A(SW, KKN, BUFN, 0)                                                             \
+  DMAX(DX, (KB) + 2)                                                                       \
+  M16_MFMA(BUF, 0)                                                                         \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                                       \
+  M16_SPREAD4                                                                              \
+  __builtin_amdgcn_sched_barrier(0);                                                       \
+  M16_READ_A(SW, KKN, BUFN, 1)                                                             \
+  DMAW(DW, (KB) + 3)                                                                       \
+  M16_MFMA(BUF, 1)                                                                         \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                       \
+  M16_SPREAD4                                                                              \
+  __builtin_amdgcn_sched_barrier(0);
 // One k-block with the pipeline of TL_STEP: k-step 0 is multiplied while k-step 1
-// is read, the wait and the barrier, the copies of KB + 2 (tokens) and KB + 3
-// (weights), then k-step 1 is multiplied while k-step 0 of KB + 1 is read.
+// is read, the wait and the barrier, then k-step 1 is multiplied while k-step 0 of
+// KB + 1 is read and the copies of KB + 2 (tokens) and KB + 3 (weights) go out.
 #define M16_STEP(KB, WS, XS, WN, XN)                                                       \
   M16_KSTEP(sW##WS, sX##XS, 1, 1, 0)                                                       \
   __builtin_amdgcn_s_waitcnt(kStepWait);                                                   \
   TILED_BARRIER()                                                                          \
-  DMAX(sX##XS, (KB) + 2)                                                                   \
-  DMAW(sW##WS, (KB) + 3)                                                                   \
-  M16_KSTEP(sW##WN, sX##XN, 0, 0, 1)
+  M16_KSTEP_COPY(sW##WN, sX##XN, 0, 0, 1, sX##XS, sW##WS, KB)
 #define M16_KLOOP(PROLOGUE_WAIT)                                                           \
   DMAW(sW0, 0)                                                                             \
   DMAX(sX0, 0)                                                                             \
