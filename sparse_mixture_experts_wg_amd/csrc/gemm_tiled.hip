@@ -235,22 +235,20 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
 // and gives the same sums to the bit: both add the products of each 16-wide half of
 // a 32-wide k-step into the accumulator in the same order.
 //
-// Weight fragment f (rows 16 f .. 16 f + 15 of the wavefront's block), k-step kk:
-// logical chunk 4 kk + (lane >> 4) of row 16 f + (lane & 15) sits at physical chunk
-// (lane >> 4) ^ swz(lane & 15) ^ 4 kk ^ (f & 1) kOddXor / 16, so every read address
-// is lane_base ^ (64 kk | (f & 1) kOddXor) + 2048 f. Token fragment t of wavefront
-// column wc holds tile rows (4 t + wc) 16 + 0..15 (the fragments are dealt to the
-// wavefronts in turn), all of one swizzle parity: lane_base ^ 64 kk + 8192 t. The
-// empty asm hands each k-step a fresh copy of the lane base, so that the compiler
-// does not keep one address register per slot, k-step and parity live across the
-// loop. NT (4 or 1) is the number of token fragments a wavefront multiplies.
+// Fragment f (weight rows 16 f .. 16 f + 15 of the wavefront's block, or tokens
+// 16 t ..), k-step kk: logical chunk 4 kk + (lane >> 4) of row 16 f + (lane & 15)
+// sits at physical chunk (lane >> 4) ^ swz(lane & 15) ^ 4 kk ^ (f & 1) kOddXor / 16,
+// so every read address is lane_base ^ (64 kk | (f & 1) kOddXor) + 2048 f. The empty
+// asm hands each k-step a fresh copy of the lane base, so that the compiler does not
+// keep one address register per slot, k-step and parity live across the loop.
 #define M16_READ_B(SX, KK, BUF)                                                            \
   {                                                                                        \
     uint32_t lb_ = laneB;                                                                  \
     asm volatile("" : "+v"(lb_));                                                          \
     const char *p0_ = reinterpret_cast<const char *>(SX) + (lb_ ^ (64 * (KK)));            \
-    _Pragma("unroll") for (int t = 0; t < kNT; ++t) fb[BUF][t] =                           \
-        *reinterpret_cast<const bf16x8 *>(p0_ + t * 8192);                                 \
+    const char *p1_ = reinterpret_cast<const char *>(SX) + (lb_ ^ (64 * (KK) + kOddXor));  \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) fb[BUF][t] =                             \
+        *reinterpret_cast<const bf16x8 *>(((t & 1) ? p1_ : p0_) + t * 2048);               \
   }
 #define M16_READ_A(SW, KK, BUF, H)                                                         \
   {                                                                                        \
@@ -263,7 +261,7 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
   }
 #define M16_MFMA(BUF, H)                                                                   \
   _Pragma("unroll") for (int f = 4 * (H); f < 4 * (H) + 4; ++f)                           \
-    _Pragma("unroll") for (int t = 0; t < kNT; ++t)                                        \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                          \
       acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[BUF][f], fb[BUF][t], acc[f][t], \
                                                           0, 0, 0);
 // Multiply the fragments in BUF while k-step KKN of (SW, SX) is read into BUFN, in
@@ -276,14 +274,14 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
   M16_READ_A(SW, KKN, BUFN, 0)                                                             \
   M16_MFMA(BUF, 0)                                                                         \
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
-  __builtin_amdgcn_sched_group_barrier(0x100, kNT + 4, 0);                                 \
-  __builtin_amdgcn_sched_group_barrier(0x008, 4 * kNT - 1, 0);                             \
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 15, 0);                                      \
   __builtin_amdgcn_sched_barrier(0);                                                       \
   M16_READ_A(SW, KKN, BUFN, 1)                                                             \
   M16_MFMA(BUF, 1)                                                                         \
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
   __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                       \
-  __builtin_amdgcn_sched_group_barrier(0x008, 4 * kNT - 1, 0);                             \
+  __builtin_amdgcn_sched_group_barrier(0x008, 15, 0);                                      \
   __builtin_amdgcn_sched_barrier(0);
 // The k-step behind a barrier, with the copies into the slots the barrier freed
 // (tokens of KB + 2 from DX, weights of KB + 3 from DW) issued one at a time between
@@ -291,32 +289,22 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
 // reaches the memory system evenly, and on MI355X both projections ran 5% faster
 // (bitwise the same sums).
 #define M16_SPREAD4                                                                        \
-  if constexpr (kNT == 1) {                                                                \
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                     \
-  } else {                                                                                 \
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                     \
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                     \
-  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
 #define M16_KSTEP_COPY(SW, SX, KKN, BUFN, BUF, DX, DW, KB)                                 \
   M16_READ_B(SX, KKN, BUFN)                                                                \
   M16_READ_A(SW, KKN, BUFN, 0)                                                             \
   DMAX(DX, (KB) + 2)                                                                       \
   M16_MFMA(BUF, 0)                                                                         \
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
-  __builtin_amdgcn_sched_group_barrier(0x100, kNT + 4, 0);                                 \
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                                       \
   M16_SPREAD4                                                                              \
   __builtin_amdgcn_sched_barrier(0);                                                       \
   M16_READ_A(SW, KKN, BUFN, 1)                                                             \
@@ -371,7 +359,7 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
 // Three weight stages and two token stages (160 KiB of LDS). The weight tile of the
 // first token block to reach a k-block is an HBM miss; about two k-blocks of lead
 // hide more of that latency than one (measured 4-9% faster than two stages of both).
-template <bool GATEUP, int NT>
+template <bool GATEUP>
 __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restrict__ X,
                                         const uint16_t *__restrict__ Wa,
                                         const uint16_t *__restrict__ Wb, void *__restrict__ out,
@@ -419,11 +407,7 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
   // weight (token) fragment, physical chunk of logical chunk lane >> 4
   const uint32_t lchunk = uint32_t(((lane >> 4) ^ swz(lane & 15)) << 4);
   const uint32_t laneA = uint32_t((wr * 128 + (lane & 15)) * 128) | lchunk;
-  // token fragment t of wavefront wc is tile rows (4 t + wc) 16 + 0..15: every such
-  // row has the swizzle parity of wc, so one base serves all of them (+ 8 KiB per t)
-  const uint32_t laneB = uint32_t((wc * 16 + (lane & 15)) * 128) |
-                         uint32_t(((lane >> 4) ^ swz(16 * (wc & 1) + (lane & 15))) << 4);
-  constexpr int kNT = NT;
+  const uint32_t laneB = uint32_t((wc * 64 + (lane & 15)) * 128) | lchunk;
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -458,13 +442,13 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
 #undef DMAW
 #undef DMAX
 
-  // ---- epilogue: lane holds token (4 t + wc) 16 + (lane & 15) and weight rows
+  // ---- epilogue: lane holds token wc * 64 + 16 t + (lane & 15) and weight rows
   // 16 f + 4 (lane >> 4) + 0..3 of the wavefront's 128; for gate-up fragments 0-3
   // are g and 4-7 the u of the same 64 columns
   const int ih = 4 * (lane >> 4);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int tok = tl.m0 + (4 * t + wc) * 16 + (lane & 15);
+  for (int t = 0; t < 4; ++t) {
+    const int tok = tl.m0 + wc * 64 + t * 16 + (lane & 15);
     if (tok >= tl.ne) continue;
     const size_t orow = size_t(tl.row0 + tok) * N + size_t(tl.ks) * size_t(part_stride);
     if constexpr (GATEUP) {
@@ -689,20 +673,17 @@ __global__ __launch_bounds__(512) void tiled128_kernel(
                                 sW2, sX0, sX1);
 }
 
-// Experts of more than a few hundred rows: 256-token tiles (body256). Every tile
-// is 256 tokens wide; an expert's last, partly filled tile skips the matrix work of
-// its empty token fragments instead. Its token fragments are dealt to the
-// wavefronts in turn (fragment t of wavefront column wc holds rows (4 t + wc) 16..),
-// so a tile with at most 64 rows left runs one fragment per wavefront on every
-// SIMD (at the 8x7B prefill shape that cuts the matrix work issued from 12.5% to
-// about 3% above the algorithmic flop; on MI355X within +-1-3% of the time of
-// computing the padding, bitwise the same sums). Narrowing each expert's last tile
-// to 64 or 128 tokens in the same launch was measured no faster and with twice the
-// HBM reads (3.1 -> 5.9 GB per gate-up launch): a narrow tail has a quarter of a
-// full tile's matrix work, runs ahead of its expert's full tiles of the same column
-// block through the k-loop and fetches the shared weight slices first, and the
-// full tiles then find them evicted from L2. Running all tails after the full
-// tiles cut that to 4.7 GB and was slower.
+// Experts of more than a few hundred rows: 256-token tiles (body256).
+// Narrowing each expert's last, partly filled tile to 64 or 128 tokens (33
+// instead of 36 full tiles' worth of matrix work at the 8x7B prefill shape)
+// was measured on MI355X, in one process, interleaved: gate-up 1.79 vs 1.81 ms
+// and down 0.95 vs 0.97 ms on the mean, no gain on the best runs, and twice
+// the HBM reads (3.1 -> 5.9 GB per gate-up launch): a narrow tail has a quarter
+// of a full tile's matrix work, runs ahead of its expert's full tiles of the
+// same column block through the k-loop and fetches the shared weight slices
+// first, and the full tiles then find them evicted from L2. Running all tails
+// after the full tiles cut that to 4.7 GB and was slower. Every tile is 256
+// tokens wide.
 template <bool GATEUP>
 __global__ __launch_bounds__(512) void tiled256_kernel(
     const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
@@ -715,14 +696,7 @@ __global__ __launch_bounds__(512) void tiled256_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t sX1[256 * 64];
   Tile tl;
   if (!find_tile<256, GATEUP ? 128 : 256>(offsets, E, N, ksplit, tl)) return;
-  // token fragments of this wavefront that hold a row of the expert: (4 t + wc) 16 <
-  // rows left in the tile; a wavefront with at most one runs the one-fragment body
-  const int wc = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3;
-  const int nt = (min(256, tl.ne - tl.m0) - 16 * wc + 63) / 64;
-  if (nt >= 2)
-    body256<GATEUP, 4>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1, sW2, sX0, sX1);
-  else
-    body256<GATEUP, 1>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1, sW2, sX0, sX1);
+  body256<GATEUP>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1, sW2, sX0, sX1);
 }
 
 // Upper bound of the tile count for any split of S rows over E experts.
