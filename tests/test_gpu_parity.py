@@ -473,9 +473,9 @@ EXPERT_CASES = [
     ("tiled_long_segments", "tiled", 4096, 256, 384, [0, 1500, 1, 384, 769, 0, 2000, 3000], 0, 1),
     ("tiled_partials2", "tiled", 4096, 2048, 512, [0, 1500, 1, 256, 769, 0, 2000, 3000], 1, 2),
     ("tiled_partials4_long", "tiled", 4096, 256, 1024, [3000, 1, 0, 257, 0, 1500, 2000, 769], 1, 4),
-    # 256-token tiles with 16..113 rows: each wavefront multiplies the token fragments
-    # that hold a row (one or all four); the counts sit on both sides of every
-    # wavefront's switch between the two
+    # 256-token tiles holding 16..113 rows: segments end on both sides of the 16-, 48-,
+    # 64- and 112-row marks (edges of 16-token fragments and of a wavefront column's
+    # 64 tokens)
     ("tiled_tail_fragments", "tiled", 600, 256, 512, [65, 112, 113, 64, 16, 17, 48, 49], 0, 1),
     ("tiled_tail_fragments_p4", "tiled", 600, 256, 512, [65, 112, 113, 64, 16, 17, 48, 49], 1,
      4),
