@@ -242,10 +242,11 @@ def main():
 
 
 def measure(workload: str, args, cpu_seconds: float) -> dict:
-    """One workload: warm-up, exactly args.steps timed steps, the dominant kernel's
-    roofline from HIP events inside the timed region, a stage breakdown pass, the
-    one-call entry point, and the CPU oracle on a bounded sample with a parity
-    spot check of the timed run's output."""
+    """One workload: warm-up, exactly args.steps timed steps (each one call of the
+    whole layer, moe_forward or moe_block_forward), the dominant kernel's roofline
+    from HIP events the library records around it inside the timed region, a stage
+    breakdown pass and a timing of the staged entry points, and the CPU oracle on a
+    bounded sample with a parity spot check of the timed run's output."""
     import numpy as np
     import torch
 
@@ -295,7 +296,24 @@ def measure(workload: str, args, cpu_seconds: float) -> dict:
     else:
         x_in = dev["x"]
 
-    def step(i, ev=None, gu=None):
+    # the timed step: one call of the whole layer (the library records the gate-up
+    # events inside it when `gu` is given)
+    if args.block:
+        ws_fwd = torch.empty((moe.block_workspace_bytes(p),), dtype=torch.uint8, device="cuda")
+    else:
+        ws_fwd = torch.empty((moe.forward_workspace_bytes(p),), dtype=torch.uint8, device="cuda")
+
+    def step(i, gu=None):
+        ws = wsets[i % copies]
+        if args.block:
+            moe.block_forward(p, h_in, norm_w, BLOCK_EPS, dev["w_g"], ws["w1"], ws["w3"], ws["w2"],
+                              y, topk_idx=idx, topk_w=w, ws=ws_fwd, events=gu)
+        else:
+            moe.forward(p, x_in, dev["w_g"], ws["w1"], ws["w3"], ws["w2"], y, topk_idx=idx,
+                        topk_w=w, ws=ws_fwd, events=gu)
+
+    # the same layer through the staged entry points, for the stage breakdown
+    def step_staged(i, ev=None):
         ws = wsets[i % copies]
         if ev is not None:
             ev[0].record()
@@ -307,14 +325,10 @@ def measure(workload: str, args, cpu_seconds: float) -> dict:
         moe.permute(p, x_in, idx, offsets, perm, slot, x_perm, gather=not rows_direct)
         if ev is not None:
             ev[1].record()
-        if gu is not None:
-            gu[0].record()
         if rows_direct:
             moe.expert_gate_up_rows(p, x_in, perm, offsets, ws["w1"], ws["w3"], act)
         else:
             moe.expert_gate_up(p, x_perm, offsets, ws["w1"], ws["w3"], act)
-        if gu is not None:
-            gu[1].record()
         if ev is not None:
             ev[2].record()
         moe.expert_down(p, act, offsets, ws["w2"], o_perm)
@@ -331,14 +345,17 @@ def measure(workload: str, args, cpu_seconds: float) -> dict:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    counts = np.diff(parity.host_array(offsets).astype(np.int64))
 
     # Timed region: exactly `steps` steps. The only events inside it bracket the
-    # dominant kernel (gate-up) on the stream it is launched on (torch's current
-    # stream, which the binding passes to the library), on every GU_EVERY-th step
-    # from the first: a pair of events costs about 6 us of a 430 us decode step.
+    # dominant kernel (gate-up): the library records them on the stream it launches
+    # on (torch's current stream, which the binding passes), on every GU_EVERY-th
+    # step from the first; a pair of events costs about 6 us of a 430 us decode
+    # step. Recording each event once beforehand creates it.
     gu_steps = list(range(0, args.steps, GU_EVERY))
     gu_events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in gu_steps}
+    for evs in gu_events.values():
+        for ev in evs:
+            ev.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -354,35 +371,28 @@ def measure(workload: str, args, cpu_seconds: float) -> dict:
     n_diag = max(3, min(args.steps, 30))
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_diag)]
     for i in range(n_diag):
-        step(i, events[i])
+        step_staged(i, events[i])
     torch.cuda.synchronize()
+    counts = np.diff(parity.host_array(offsets).astype(np.int64))
     stage = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(4)] for ev in events])
     stage_ms = stage.mean(axis=0)
     norm_ms = float(np.mean([ev[0].elapsed_time(ev[5]) for ev in events])) if args.block else None
     step_ms = np.array([ev[0].elapsed_time(ev[4]) for ev in events])
     gpu_ms_step = float(np.mean(step_ms))
 
-    # one-call API on the same inputs, for comparison (not part of the timed region)
-    if args.block:
-        ws_fwd = torch.empty((moe.block_workspace_bytes(p),), dtype=torch.uint8, device="cuda")
-
-        def one_call(ws_):
-            moe.block_forward(p, h_in, norm_w, BLOCK_EPS, dev["w_g"], ws_["w1"], ws_["w3"],
-                              ws_["w2"], y, ws=ws_fwd)
-    else:
-        ws_fwd = torch.empty((moe.forward_workspace_bytes(p),), dtype=torch.uint8, device="cuda")
-
-        def one_call(ws_):
-            moe.forward(p, dev["x"], dev["w_g"], ws_["w1"], ws_["w3"], ws_["w2"], y, ws=ws_fwd)
-    for _ in range(3):
-        one_call(wsets[0])
+    # the staged entry points, one call per stage, for comparison (not part of the
+    # timed region)
+    n_st = max(5, min(args.steps, 50))
     torch.cuda.synchronize()
-    n_fwd = max(5, min(args.steps, 50))
     t1 = time.perf_counter()
-    for i in range(n_fwd):
-        one_call(wsets[i % copies])
+    for i in range(n_st):
+        step_staged(i)
     torch.cuda.synchronize()
-    ms_forward = (time.perf_counter() - t1) * 1e3 / n_fwd
+    ms_staged = (time.perf_counter() - t1) * 1e3 / n_st
+    # the timed run's output again for the spot check below (the staged passes
+    # write the same buffers with bitwise the same values)
+    step(0)
+    torch.cuda.synchronize()
 
     # ---- roofline of the dominant kernel (gate-up) --------------------------------
     es = 2 if cfg.dtype == "bf16" else 4
@@ -516,7 +526,7 @@ def measure(workload: str, args, cpu_seconds: float) -> dict:
             "frac_of_hbm_peak": round((T * d * es * 2 + d * es) / (norm_ms / 1e3) / 1e9
                                       / HBM_PEAK_GBS, 4)},
         "stages_note": f"separate pass of {n_diag} steps with events between the stages",
-        "ms_per_step_one_call_api": round(ms_forward, 5),
+        "ms_per_step_staged_api": round(ms_staged, 5),
         "rows_per_expert": counts.tolist(),
         "parity_spot_check": spot,
     }

@@ -292,6 +292,23 @@ moe_status moe_forward(const moe_problem *p, const void *x, const void *w_g, con
                        const void *w3, const void *w2, void *y, int32_t *topk_idx,
                        float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * moe_forward and moe_block_forward for profiling callers: the same layer,
+ * bitwise the same results, plus two HIP events (hipEvent_t, created by the
+ * caller, NULL for none) recorded on `stream` right before and right after the
+ * launch of the expert gate-up (the layer's dominant kernel), so that its time
+ * inside a stream of whole-layer calls can be read with hipEventElapsedTime.
+ */
+moe_status moe_forward_profiled(const moe_problem *p, const void *x, const void *w_g,
+                                const void *w1, const void *w3, const void *w2, void *y,
+                                int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                                void *stream, void *gate_up_begin, void *gate_up_end);
+moe_status moe_block_forward_profiled(const moe_problem *p, const void *h, const void *norm_w,
+                                      float eps, const void *w_g, const void *w1, const void *w3,
+                                      const void *w2, void *y, int32_t *topk_idx, float *topk_w,
+                                      void *ws, size_t ws_bytes, void *stream,
+                                      void *gate_up_begin, void *gate_up_end);
+
 /* Size of the static scratch array moe_forward_noalloc uses as its workspace. */
 #define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
 

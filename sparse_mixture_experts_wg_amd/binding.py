@@ -105,11 +105,14 @@ def _load() -> ctypes.CDLL:
         "moe_combine": ([P, vp, vp, vp, vp, vp], i32),
         "moe_forward_workspace_bytes": ([P], sz),
         "moe_forward": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_forward_profiled": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp], i32),
         "moe_rmsnorm": ([P, vp, vp, ctypes.c_float, vp, vp], i32),
         "moe_combine_residual": ([P, vp, vp, vp, vp, vp, vp], i32),
         "moe_block_workspace_bytes": ([P], sz),
         "moe_block_forward": ([P, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
                               i32),
+        "moe_block_forward_profiled": ([P, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        sz, vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -322,8 +325,8 @@ def combine_residual(p: Problem, o_perm, slot_pos, topk_w, residual, y=None, str
 
 
 def block_forward(p: Problem, h, norm_w, eps: float, w_g, w1, w3, w2, y=None, topk_idx=None,
-                  topk_w=None, ws=None, stream=None):
-    """Pre-norm block: y = h + MoE(RMSNorm(h) * norm_w)."""
+                  topk_w=None, ws=None, stream=None, events=None):
+    """Pre-norm block: y = h + MoE(RMSNorm(h) * norm_w); `events` as for forward."""
     torch = _torch()
     T, d, hd, E, K = int(p.T), int(p.d), int(p.h), int(p.E), int(p.K)
     dt = _tdtype(p.dtype)
@@ -331,14 +334,16 @@ def block_forward(p: Problem, h, norm_w, eps: float, w_g, w1, w3, w2, y=None, to
     y = _empty((T, d), yd, h) if y is None else y
     need = block_workspace_bytes(p)
     ws = _empty((max(need, 1),), torch.uint8, h) if ws is None else ws
-    _check(lib.moe_block_forward(ctypes.byref(p), _ptr(h, "h", (T, d), dt),
-                                 _ptr(norm_w, "norm_w", (d,), dt), ctypes.c_float(eps),
-                                 _ptr(w_g, "w_g", (d, E), dt), _ptr(w1, "w1", (E, hd, d), dt),
-                                 _ptr(w3, "w3", (E, hd, d), dt), _ptr(w2, "w2", (E, d, hd), dt),
-                                 _ptr(y, "y", (T, d), yd),
-                                 _ptr(topk_idx, "topk_idx", (T, K), torch.int32),
-                                 _ptr(topk_w, "topk_w", (T, K), torch.float32), _ptr(ws, "ws"),
-                                 ws.numel() * ws.element_size(), _stream(stream)))
+    args = (ctypes.byref(p), _ptr(h, "h", (T, d), dt), _ptr(norm_w, "norm_w", (d,), dt),
+            ctypes.c_float(eps), _ptr(w_g, "w_g", (d, E), dt), _ptr(w1, "w1", (E, hd, d), dt),
+            _ptr(w3, "w3", (E, hd, d), dt), _ptr(w2, "w2", (E, d, hd), dt),
+            _ptr(y, "y", (T, d), yd), _ptr(topk_idx, "topk_idx", (T, K), torch.int32),
+            _ptr(topk_w, "topk_w", (T, K), torch.float32), _ptr(ws, "ws"),
+            ws.numel() * ws.element_size(), _stream(stream))
+    if events is None:
+        _check(lib.moe_block_forward(*args))
+    else:
+        _check(lib.moe_block_forward_profiled(*args, *_events(events)))
     return y
 
 
@@ -354,8 +359,21 @@ def combine(p: Problem, o_perm, slot_pos, topk_w, y=None, stream=None):
     return y
 
 
+def _events(events):
+    """(begin, end) torch.cuda.Event pair -> two raw hipEvent_t handles (the events
+    must have been recorded once, which creates them), or two NULLs."""
+    if events is None:
+        return None, None
+    handles = [int(ev.cuda_event) for ev in events]
+    if len(handles) != 2 or not all(handles):
+        raise ValueError("events: a pair of torch.cuda.Event that have been recorded once")
+    return ctypes.c_void_p(handles[0]), ctypes.c_void_p(handles[1])
+
+
 def forward(p: Problem, x, w_g, w1, w3, w2, y=None, topk_idx=None, topk_w=None, ws=None,
-            stream=None):
+            stream=None, events=None):
+    """The whole layer (moe_forward); with `events` (a pair of recorded
+    torch.cuda.Event) moe_forward_profiled, which records them around the gate-up."""
     torch = _torch()
     T, d, h, E, K = int(p.T), int(p.d), int(p.h), int(p.E), int(p.K)
     dt = _tdtype(p.dtype)
@@ -363,12 +381,16 @@ def forward(p: Problem, x, w_g, w1, w3, w2, y=None, topk_idx=None, topk_w=None, 
     y = _empty((T, d), yd, x) if y is None else y
     need = forward_workspace_bytes(p)
     ws = _empty((max(need, 1),), torch.uint8, x) if ws is None else ws
-    _check(lib.moe_forward(ctypes.byref(p), _ptr(x, "x", (T, d), dt), _ptr(w_g, "w_g", (d, E), dt),
-                           _ptr(w1, "w1", (E, h, d), dt), _ptr(w3, "w3", (E, h, d), dt),
-                           _ptr(w2, "w2", (E, d, h), dt), _ptr(y, "y", (T, d), yd),
-                           _ptr(topk_idx, "topk_idx", (T, K), torch.int32),
-                           _ptr(topk_w, "topk_w", (T, K), torch.float32), _ptr(ws, "ws"),
-                           ws.numel() * ws.element_size(), _stream(stream)))
+    args = (ctypes.byref(p), _ptr(x, "x", (T, d), dt), _ptr(w_g, "w_g", (d, E), dt),
+            _ptr(w1, "w1", (E, h, d), dt), _ptr(w3, "w3", (E, h, d), dt),
+            _ptr(w2, "w2", (E, d, h), dt), _ptr(y, "y", (T, d), yd),
+            _ptr(topk_idx, "topk_idx", (T, K), torch.int32),
+            _ptr(topk_w, "topk_w", (T, K), torch.float32), _ptr(ws, "ws"),
+            ws.numel() * ws.element_size(), _stream(stream))
+    if events is None:
+        _check(lib.moe_forward(*args))
+    else:
+        _check(lib.moe_forward_profiled(*args, *_events(events)))
     return y
 
 

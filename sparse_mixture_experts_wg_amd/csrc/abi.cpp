@@ -328,10 +328,13 @@ struct NormIn {
 
 // The whole layer on checked arguments; `residual` (nullable) is added to y;
 // with `norm`, x is first computed from norm->h (fused into the route step).
+// ev_gu0 / ev_gu1 (nullable): HIP events recorded on the stream right before and
+// right after the gate-up launch (the profiled entry points).
 moe_status run_layer(const moe_problem *p, const void *x, const void *w_g, const void *w1,
                      const void *w3, const void *w2, const void *residual, void *y,
                      int32_t *topk_idx, float *topk_w, void *ws, void *stream,
-                     const NormIn *norm = nullptr) {
+                     const NormIn *norm = nullptr, hipEvent_t ev_gu0 = nullptr,
+                     hipEvent_t ev_gu1 = nullptr) {
   const ForwardLayout L = forward_layout(p);
   char *base = static_cast<char *>(ws);
   int32_t *idx = topk_idx ? topk_idx : reinterpret_cast<int32_t *>(base + L.idx);
@@ -354,10 +357,14 @@ moe_status run_layer(const moe_problem *p, const void *x, const void *w_g, const
     // the bf16 gate-up kernels read each token row of x through perm_token, so
     // the layer needs no gathered copy of x
     CHECK(do_permute(p, x, idx, offsets, perm, slot, nullptr, s));
+    if (ev_gu0) CHECK(hip_result(hipEventRecord(ev_gu0, s), "event record"));
     CHECK(do_gate_up(p, x, offsets, w1, w3, act, s, perm));
+    if (ev_gu1) CHECK(hip_result(hipEventRecord(ev_gu1, s), "event record"));
   } else {
     CHECK(do_permute(p, x, idx, offsets, perm, slot, x_perm, s));
+    if (ev_gu0) CHECK(hip_result(hipEventRecord(ev_gu0, s), "event record"));
     CHECK(do_gate_up(p, x_perm, offsets, w1, w3, act, s));
+    if (ev_gu1) CHECK(hip_result(hipEventRecord(ev_gu1, s), "event record"));
   }
   CHECK(do_down(p, act, offsets, w2, o_perm, L.parts, s));
   CHECK(do_combine(p, o_perm, L.parts, slot, w, residual, y, s));
@@ -538,9 +545,10 @@ size_t moe_forward_workspace_bytes(const moe_problem *p) {
   return forward_layout(p).total;
 }
 
-moe_status moe_forward(const moe_problem *p, const void *x, const void *w_g, const void *w1,
-                       const void *w3, const void *w2, void *y, int32_t *topk_idx, float *topk_w,
-                       void *ws, size_t ws_bytes, void *stream) {
+moe_status moe_forward_profiled(const moe_problem *p, const void *x, const void *w_g,
+                                const void *w1, const void *w3, const void *w2, void *y,
+                                int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                                void *stream, void *gate_up_begin, void *gate_up_end) {
   return guarded([&] {
     CHECK(check_problem(p));
     CHECK(check_ptr(x, "x"));
@@ -548,8 +556,16 @@ moe_status moe_forward(const moe_problem *p, const void *x, const void *w_g, con
     if (ws_bytes < forward_layout(p).total)
       return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes,
                   forward_layout(p).total);
-    return run_layer(p, x, w_g, w1, w3, w2, nullptr, y, topk_idx, topk_w, ws, stream);
+    return run_layer(p, x, w_g, w1, w3, w2, nullptr, y, topk_idx, topk_w, ws, stream, nullptr,
+                     static_cast<hipEvent_t>(gate_up_begin), static_cast<hipEvent_t>(gate_up_end));
   });
+}
+
+moe_status moe_forward(const moe_problem *p, const void *x, const void *w_g, const void *w1,
+                       const void *w3, const void *w2, void *y, int32_t *topk_idx, float *topk_w,
+                       void *ws, size_t ws_bytes, void *stream) {
+  return moe_forward_profiled(p, x, w_g, w1, w3, w2, y, topk_idx, topk_w, ws, ws_bytes, stream,
+                              nullptr, nullptr);
 }
 
 moe_status moe_rmsnorm(const moe_problem *p, const void *h, const void *norm_w, float eps,
@@ -590,6 +606,15 @@ moe_status moe_block_forward(const moe_problem *p, const void *h, const void *no
                              const void *w_g, const void *w1, const void *w3, const void *w2,
                              void *y, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                              void *stream) {
+  return moe_block_forward_profiled(p, h, norm_w, eps, w_g, w1, w3, w2, y, topk_idx, topk_w, ws,
+                                    ws_bytes, stream, nullptr, nullptr);
+}
+
+moe_status moe_block_forward_profiled(const moe_problem *p, const void *h, const void *norm_w,
+                                      float eps, const void *w_g, const void *w1, const void *w3,
+                                      const void *w2, void *y, int32_t *topk_idx, float *topk_w,
+                                      void *ws, size_t ws_bytes, void *stream,
+                                      void *gate_up_begin, void *gate_up_end) {
   return guarded([&] {
     CHECK(check_problem(p));
     CHECK(check_eps(eps));
@@ -602,7 +627,8 @@ moe_status moe_block_forward(const moe_problem *p, const void *h, const void *no
     // the normalised input x lives after the layer's own workspace
     void *x = static_cast<char *>(ws) + forward_layout(p).total;
     const NormIn norm{h, norm_w, eps};
-    return run_layer(p, x, w_g, w1, w3, w2, h, y, topk_idx, topk_w, ws, stream, &norm);
+    return run_layer(p, x, w_g, w1, w3, w2, h, y, topk_idx, topk_w, ws, stream, &norm,
+                     static_cast<hipEvent_t>(gate_up_begin), static_cast<hipEvent_t>(gate_up_end));
   });
 }
 

@@ -605,11 +605,13 @@ def test_combine_adds_partials(moe):
     assert np.max(np.abs(y - ref)) <= 1e-6 * np.max(np.abs(ref))
 
 
-@pytest.mark.parametrize("T,cap", [(40, 0), (100, 0), (60, 9)])
+@pytest.mark.parametrize("T,cap", [(40, 0), (100, 0), (60, 9), (1, 0), (16, 0), (32, 0),
+                                   (32, 5), (20, 3)])
 def test_stream_forward_equals_staged(moe, T, cap):
     """On the streaming path moe_forward reads the token rows of x through perm_token
     instead of a gathered copy; the staged entry points gather with moe_permute.
-    Same kernels otherwise: bit-identical outputs (also under a capacity cap)."""
+    Same kernels otherwise: bit-identical outputs (also under a capacity cap), from
+    one token to well past the one-wavefront sort's 64 slots."""
     cfg = mi.Config("sf", T=T, d=256, h=384, wg_std="fan_in_d")
     inp = mi.make_inputs(cfg, seed=12)
     p = moe.problem(T, cfg.d, cfg.h, cfg.E, cfg.K, "bf16", "f32", "stream", 0, cap)
@@ -622,6 +624,36 @@ def test_stream_forward_equals_staged(moe, T, cap):
     y = moe.combine(p, o, slot, w)
     torch.cuda.synchronize()
     assert np.array_equal(parity.host_array(y), parity.host_array(y_fwd))
+
+
+@pytest.mark.parametrize("T,path", [(32, "stream"), (300, "tiled")])
+def test_forward_profiled_equals_forward(moe, T, path):
+    """moe_forward_profiled / moe_block_forward_profiled: bitwise the results of
+    moe_forward / moe_block_forward, and the two events they record around the
+    gate-up launch bracket a positive time."""
+    cfg = mi.Config("fp", T=T, d=256, h=384, wg_std="fan_in_d")
+    inp = mi.make_inputs(cfg, seed=21)
+    blk = mi.make_block(cfg, seed=22)
+    p = moe.problem(T, cfg.d, cfg.h, cfg.E, cfg.K, "bf16", "f32", path, moe.FLAG_DOWN_PARTIALS)
+    dev = parity.upload_inputs(inp, "bf16")
+    h_in = parity.device_array(blk["h"], "bf16")
+    g = parity.device_array(blk["norm_w"], "bf16")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    y0 = moe.forward(p, dev["x"], dev["w_g"], dev["w1"], dev["w3"], dev["w2"])
+    y1 = moe.forward(p, dev["x"], dev["w_g"], dev["w1"], dev["w3"], dev["w2"], events=ev[:2])
+    b0 = moe.block_forward(p, h_in, g, 1e-5, dev["w_g"], dev["w1"], dev["w3"], dev["w2"])
+    b1 = moe.block_forward(p, h_in, g, 1e-5, dev["w_g"], dev["w1"], dev["w3"], dev["w2"],
+                           events=ev[2:])
+    torch.cuda.synchronize()
+    assert np.array_equal(parity.host_array(y0), parity.host_array(y1))
+    assert np.array_equal(parity.host_array(b0), parity.host_array(b1))
+    assert ev[0].elapsed_time(ev[1]) > 0 and ev[2].elapsed_time(ev[3]) > 0
+    with pytest.raises(ValueError):
+        moe.forward(p, dev["x"], dev["w_g"], dev["w1"], dev["w3"], dev["w2"],
+                    events=[torch.cuda.Event(enable_timing=True)] * 2)
 
 
 def test_staged_with_partials_equals_forward(moe, oracle):
