@@ -16,7 +16,8 @@
 // and the slot positions are collected there and written back coalesced (each
 // thread's contiguous slot range would otherwise make every wavefront access
 // touch 64 separate lines); up to 16384 slots the sorted-row -> token map is
-// assembled in LDS too instead of being scattered to global memory.
+// assembled in LDS too, above that a second kernel over the whole GPU scatters it
+// from the slot positions (scatter_perm).
 // With a capacity C (the capacity variant) a slot whose rank within its expert
 // is C or more is dropped (slot_pos -1, no row) and the offsets count the kept
 // rows min(n_e, C) only.
@@ -36,6 +37,12 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWavesPerBlock = kThreads / 64;
 constexpr int kStage = 32768;  // slots staged in LDS (128 KiB)
+// Thread i owns the contiguous slots [i*c, (i+1)*c), so the lanes of a wavefront read
+// slots c apart: LDS holds slot s at pad(s) = s + s / 32, which puts the slots of a
+// wavefront's 64 lanes on distinct banks for any c <= 32 (one int of padding per 32).
+__device__ __forceinline__ int64_t pad(int64_t s) { return s + (s >> 5); }
+constexpr int kStagePadded = kStage + kStage / 32;
+constexpr int kPermOff = kStage / 2 + kStage / 64;  // sorted-row map after the slots
 
 __global__ __launch_bounds__(kThreads) void permute_index_kernel(
     const int32_t *__restrict__ idx, int64_t S, int K, int E, int capacity,
@@ -44,9 +51,9 @@ __global__ __launch_bounds__(kThreads) void permute_index_kernel(
   __shared__ int32_t wave_tot[kWavesPerBlock][8];
   __shared__ int32_t wave_pre[kWavesPerBlock][8];
   __shared__ int32_t expert_off[9];
-  // expert ids, then slot positions (S <= kStage); with S <= kStage / 2 the
-  // second half holds the sorted-row -> token map
-  __shared__ int32_t sidx[kStage];
+  // expert ids, then slot positions (S <= kStage, at pad(s)); with S <= kStage / 2
+  // the sorted-row -> token map follows at kPermOff
+  __shared__ int32_t sidx[kStagePadded];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -56,12 +63,9 @@ __global__ __launch_bounds__(kThreads) void permute_index_kernel(
   // (small batches skip the staging: a few slots per thread gain nothing from it)
   const bool staged = S >= 2048 && S <= kStage;
   const bool staged_perm = staged && S <= kStage / 2;
-  int32_t *sperm = sidx + kStage / 2;
+  int32_t *sperm = sidx + kPermOff;
   if (staged) {
-    const int64_t S4 = S & ~int64_t(3);
-    for (int64_t i = int64_t(tid) * 4; i < S4; i += 4 * kThreads)
-      *reinterpret_cast<int4 *>(sidx + i) = *reinterpret_cast<const int4 *>(idx + i);
-    for (int64_t i = S4 + tid; i < S; i += kThreads) sidx[i] = idx[i];
+    for (int64_t i = tid; i < S; i += kThreads) sidx[pad(i)] = idx[i];
     __syncthreads();
   }
 
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void permute_index_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) cnt[e] = 0;
   for (int64_t s = s0; s < s1; ++s) {
-    const int e = staged ? sidx[s] : idx[s];
+    const int e = staged ? sidx[pad(s)] : idx[s];
 #pragma unroll
     for (int q = 0; q < 8; ++q) cnt[q] += (q == e && q < E) ? 1 : 0;
   }
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void permute_index_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) rank[e] = wave_pre[wave][e] + incl[e] - cnt[e];
   for (int64_t s = s0; s < s1; ++s) {
-    const int e = staged ? sidx[s] : idx[s];
+    const int e = staged ? sidx[pad(s)] : idx[s];
     int p = -1;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -127,22 +131,21 @@ __global__ __launch_bounds__(kThreads) void permute_index_kernel(
       }
     }
     if (staged)
-      sidx[s] = p;  // this thread's own slot: no other thread reads it
+      sidx[pad(s)] = p;  // this thread's own slot: no other thread reads it
     else
       slot_pos[s] = p;
+    // rows -> tokens: in LDS from 2048 to kStage / 2 slots, straight to memory below,
+    // above left to scatter_perm_kernel, which spreads the scatter over the GPU
     if (p >= 0) {
       if (staged_perm)
         sperm[p] = int32_t(s / K);
-      else
+      else if (S <= kStage / 2)
         perm_token[p] = int32_t(s / K);
     }
   }
   if (staged) {
     __syncthreads();
-    const int64_t S4 = S & ~int64_t(3);
-    for (int64_t i = int64_t(tid) * 4; i < S4; i += 4 * kThreads)
-      *reinterpret_cast<int4 *>(slot_pos + i) = *reinterpret_cast<const int4 *>(sidx + i);
-    for (int64_t i = S4 + tid; i < S; i += kThreads) slot_pos[i] = sidx[i];
+    for (int64_t i = tid; i < S; i += kThreads) slot_pos[i] = sidx[pad(i)];
     if (staged_perm) {
       // rows [0, offsets[E]) exist; the rest of perm_token is left as it was
       const int64_t R = expert_off[E];
@@ -181,6 +184,17 @@ __global__ __launch_bounds__(64) void permute_index_small_kernel(
   if (p >= 0) perm_token[p] = lane / K;
 }
 
+// perm_token[slot_pos[s]] = s / K over the whole grid, for batches whose
+// sorted-row -> token map does not fit the sort's LDS (every row is written once).
+__global__ __launch_bounds__(256) void scatter_perm_kernel(const int32_t *__restrict__ slot_pos,
+                                                           int64_t S, int K,
+                                                           int32_t *__restrict__ perm_token) {
+  const int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (s >= S) return;
+  const int p = slot_pos[s];
+  if (p >= 0) perm_token[p] = int32_t(s / K);
+}
+
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restrict__ x,
                                                           const int32_t *__restrict__ perm_token,
                                                           const int32_t *__restrict__ offsets,
@@ -203,9 +217,13 @@ hipError_t launch_permute_index(const int32_t *idx, int64_t S, int K, int E, int
   if (S <= kSmallSlots)
     hipLaunchKernelGGL(permute_index_small_kernel, dim3(1), dim3(64), 0, s, idx, int(S), K, E,
                        capacity, offsets, perm_token, slot_pos);
-  else
+  else {
     hipLaunchKernelGGL(permute_index_kernel, dim3(1), dim3(kThreads), 0, s, idx, S, K, E,
                        capacity, offsets, perm_token, slot_pos);
+    if (S > kStage / 2)
+      hipLaunchKernelGGL(scatter_perm_kernel, dim3(unsigned((S + 255) / 256)), dim3(256), 0, s,
+                         slot_pos, S, K, perm_token);
+  }
   return hipGetLastError();
 }
 
