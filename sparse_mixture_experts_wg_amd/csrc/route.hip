@@ -5,8 +5,8 @@
 // x . W_gate of shape [tokens, 8]; keep the top 2 and renormalise with a
 // softmax) and notion page, sparse-gating equation G(x) = Softmax(TopK(x . W_g)).
 //
-// Layout of the work: a workgroup owns TPB tokens (1 up to 1024 tokens, else 2:
-// measured fastest on MI355X from T = 1 to 16384) and its 4
+// Layout of the work: a workgroup owns TPB tokens (1 up to 1024 tokens, else 2;
+// bf16 batches of 8 experts from 2048 tokens on take route_wide_kernel below) and its 4
 // wavefronts split the dot products into quarters of d, so that even a 1-token
 // batch keeps 4 wavefronts of loads in flight. Within its quarter a wavefront
 // takes 512 rows j at a time, lane L the rows j0 + 64 r + L (r = 0..7): each
@@ -178,6 +178,85 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ x,
   topk_out(total, t, tok0 + t, E, K, idx, w, logits);
 }
 
+// Large batches, bf16 and 8 experts: route_kernel re-reads all of W_g (16 bytes
+// per row of d) from L2 for every 1-2 tokens and loads x 2 bytes per lane, so at
+// thousands of tokens it moves about five times the bytes of x through L2 and
+// issues one load instruction per 128 bytes of x. Here a workgroup takes
+// kWideTPB = 8 tokens and a lane 8 consecutive rows j .. j + 7 of its quarter of d:
+// one 16-byte load per token and 512-row block brings x[t][j .. j + 7], and the
+// 8 x 8 weights of those rows (8 loads of one W_g row each) serve all 8 tokens.
+// The 64 partial sums per lane (8 tokens x 8 experts) are reduced over the
+// wavefront by halving exchanges (at the exchange with lane ^ m a lane keeps the
+// half of its values selected by bit m of its index and adds its partner's copy
+// of that half; after m = 32 .. 1 lane L holds sum L = token L / 8, expert L % 8),
+// then over the 4 quarters in LDS in the order 0+1+2+3.
+constexpr int kWideTPB = 8;
+
+__global__ __launch_bounds__(256) void route_wide_kernel(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ wg,
+                                                        int64_t T, int d, int K,
+                                                        int32_t *__restrict__ idx,
+                                                        float *__restrict__ w,
+                                                        float *__restrict__ logits) {
+  __shared__ float part[kWaves][64];
+  __shared__ float total[64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t tok0 = int64_t(blockIdx.x) * kWideTPB;
+  const int ntok = int(min(int64_t(kWideTPB), T - tok0));
+
+  float v[64];  // [token * 8 + expert]
+#pragma unroll
+  for (int i = 0; i < 64; ++i) v[i] = 0.f;
+
+  // d / 4 is a multiple of 32, so a lane's 8 rows are all inside the quarter or
+  // all outside it
+  const int rbeg = wave * (d >> 2), rend = rbeg + (d >> 2);
+  for (int j0 = rbeg; j0 < rend; j0 += 512) {
+    const int j = j0 + 8 * lane;
+    if (j >= rend) continue;
+    u32x4 xq[kWideTPB];
+#pragma unroll
+    for (int t = 0; t < kWideTPB; ++t)  // a missing token re-reads the last one
+      xq[t] = *reinterpret_cast<const u32x4 *>(x + (tok0 + min(t, ntok - 1)) * d + j);
+    float wv[8][8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) load8<true>(wg, int64_t(j + r) * 8, wv[r]);
+#pragma unroll
+    for (int t = 0; t < kWideTPB; ++t) {
+      if (t >= ntok) continue;
+      float xv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[2 * i] = __uint_as_float(xq[t][i] << 16);
+        xv[2 * i + 1] = __uint_as_float(xq[t][i] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[t * 8 + e] = fmaf(xv[r], wv[r][e], v[t * 8 + e]);
+    }
+  }
+
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const bool hi = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < m; ++i) {
+      const float send = hi ? v[i] : v[i + m];
+      const float keep = hi ? v[i + m] : v[i];
+      v[i] = keep + __shfl_xor(send, m, 64);
+    }
+  }
+  part[wave][lane] = v[0];
+  __syncthreads();
+  if (wave == 0) total[lane] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t >= ntok) return;
+  topk_out(total, t, tok0 + t, 8, K, idx, w, logits);
+}
+
 // The pre-norm block's RMSNorm fused in front of the router: x = RMSNorm(h) * g
 // is computed, written (the expert path reads it) and routed in one pass. The
 // mean square of each token follows norm.hip's order exactly (thread i sums the
@@ -297,10 +376,22 @@ __global__ __launch_bounds__(256) void norm_route_kernel(
   topk_out(total, t, tok0 + t, E, K, idx, w, logits);
 }
 
+// From this many tokens on, bf16 batches with 8 experts take route_wide_kernel
+// (MI355X, d = 4096 and 6144, x resident in the last-level cache: equal at 2048
+// tokens, 15.4 -> 11.2 us at 4096 and 49.6 -> 40.6 us at 16384 for d = 4096; below
+// 2048 tokens its fewer workgroups lose, 8.3 against 6.5 us at 1024). Variants
+// measured no better: the next 512-row block's loads issued before the current
+// block's arithmetic, and 4 or 2 tokens per workgroup.
+constexpr int64_t kWideMinT = 2048;
+
 template <bool BF16, bool E8>
 void launch(hipStream_t s, const void *x, const void *wg, int64_t T, int d, int E, int K,
             int32_t *idx, float *w, float *logits) {
-  if (T <= 1024)
+  if (BF16 && E8 && T >= kWideMinT)
+    hipLaunchKernelGGL(route_wide_kernel, dim3(unsigned((T + kWideTPB - 1) / kWideTPB)),
+                       dim3(256), 0, s, static_cast<const uint16_t *>(x),
+                       static_cast<const uint16_t *>(wg), T, d, K, idx, w, logits);
+  else if (T <= 1024)
     hipLaunchKernelGGL((route_kernel<BF16, E8, 1>), dim3(unsigned(T)), dim3(256), 0, s, x, wg, T,
                        d, E, K, idx, w, logits);
   else
@@ -309,15 +400,25 @@ void launch(hipStream_t s, const void *x, const void *wg, int64_t T, int d, int 
 }
 
 template <bool BF16, bool E8>
-void launch_nr(hipStream_t s, const void *h, const void *g, float eps, const void *wg, int64_t T,
-               int d, int E, int K, void *x, int32_t *idx, float *w) {
-  // tokens per workgroup as the router alone
-  if (T <= 1024)
+hipError_t launch_nr(hipStream_t s, const void *h, const void *g, float eps, const void *wg,
+                     int64_t T, int d, int E, int K, void *x, int32_t *idx, float *w) {
+  // tokens per workgroup as the router alone; where the router alone runs
+  // route_wide_kernel, the norm and that router run as two launches (bitwise the
+  // staged moe_rmsnorm + moe_route)
+  if (BF16 && E8 && T >= kWideMinT) {
+    const hipError_t e = launch_rmsnorm(true, h, g, eps, T, d, x, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(route_wide_kernel, dim3(unsigned((T + kWideTPB - 1) / kWideTPB)),
+                       dim3(256), 0, s, static_cast<const uint16_t *>(x),
+                       static_cast<const uint16_t *>(wg), T, d, K, idx, w, nullptr);
+  } else if (T <= 1024) {
     hipLaunchKernelGGL((norm_route_kernel<BF16, E8, 1>), dim3(unsigned(T)), dim3(256), 0, s, h, g,
                        eps, wg, T, d, E, K, x, idx, w, nullptr);
-  else
+  } else {
     hipLaunchKernelGGL((norm_route_kernel<BF16, E8, 2>), dim3(unsigned((T + 1) / 2)), dim3(256),
                        0, s, h, g, eps, wg, T, d, E, K, x, idx, w, nullptr);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -336,11 +437,10 @@ hipError_t launch_norm_route(bool bf16, const void *h, const void *g, float eps,
                              int64_t T, int d, int E, int K, void *x, int32_t *idx, float *w,
                              hipStream_t s) {
   const bool e8 = (E == 8);
-  if (bf16 && e8) launch_nr<true, true>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
-  else if (bf16) launch_nr<true, false>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
-  else if (e8) launch_nr<false, true>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
-  else launch_nr<false, false>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
-  return hipGetLastError();
+  if (bf16 && e8) return launch_nr<true, true>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
+  if (bf16) return launch_nr<true, false>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
+  if (e8) return launch_nr<false, true>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
+  return launch_nr<false, false>(s, h, g, eps, wg, T, d, E, K, x, idx, w);
 }
 
 }  // namespace moe

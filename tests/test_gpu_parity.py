@@ -276,12 +276,17 @@ def test_forward_large_batch(moe, oracle):
 
 # ---- single steps ------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", WORKLOADS + ["small_E3", "odd_T1501_d384", "f32_E5_d640"])
+@pytest.mark.parametrize("name", WORKLOADS + ["small_E3", "odd_T1501_d384", "odd_T2053_d384",
+                                               "bf16_E6_T1100", "f32_E5_d640"])
 def test_route_step(moe, oracle, name):
     if name == "small_E3":
         cfg = mi.Config("r", T=517, d=256, h=128, E=3, K=2, wg_std="fan_in_d")
+    elif name == "odd_T2053_d384":  # 8 tokens per workgroup (5 in the last), 96-row quarters
+        cfg = mi.Config("r", T=2053, d=384, h=128, wg_std="fan_in_d")
     elif name == "odd_T1501_d384":  # 2 tokens per workgroup, a ragged 512-row block
         cfg = mi.Config("r", T=1501, d=384, h=128, wg_std="fan_in_d")
+    elif name == "bf16_E6_T1100":  # 2 tokens per workgroup (fewer than 8 experts)
+        cfg = mi.Config("r", T=1101, d=384, h=128, E=6, K=2, wg_std="fan_in_d")
     elif name == "f32_E5_d640":
         cfg = mi.Config("r", T=2049, d=640, h=128, E=5, K=2, dtype="f32", wg_std="fan_in_d")
     else:
@@ -308,15 +313,19 @@ PERMUTE_CASES = [
     ("one_expert", 100, 1, 1),
     ("k1", 777, 8, 1),
     ("big", 40000, 8, 2),
-    # the index kernel stages slots in LDS from 2048 up to 32768 slots, and the
-    # row -> token map as well up to 16384: both sides of each boundary
-    # up to 64 slots one wavefront sorts them (a decode batch: T = 32, K = 2)
+    # up to 64 slots one wavefront sorts them (a decode batch: T = 32, K = 2), up
+    # to 5119 one workgroup (staging slots and row map in LDS from 2048 on), from
+    # 5120 a grid of workgroups of 2048-slot ranges (a ragged last range, and one
+    # workgroup per 1/64 of the slots past 131072): both sides of each boundary
     ("slots_64", 32, 8, 2),
     ("slots_63", 63, 8, 1),
     ("slots_65", 65, 8, 1),
     ("slots_42_E3", 21, 3, 2),
     ("slots_2047", 2047, 8, 1),
     ("slots_2048", 1024, 8, 2),
+    ("slots_5119", 5119, 8, 1),
+    ("slots_5120", 2560, 8, 2),
+    ("slots_6001_E5", 6001, 5, 1),
     ("slots_16384", 8192, 8, 2),
     ("slots_16385", 16385, 5, 1),
     ("slots_20000", 10000, 8, 2),
@@ -758,13 +767,17 @@ def test_block_forward(moe, oracle, name, cfg, path):
 
 @pytest.mark.parametrize("T,d,dtype,E", [
     (250, 256, "bf16", 8), (700, 256, "bf16", 8), (1501, 256, "bf16", 8),
-    (300, 128, "f32", 8), (90, 256, "bf16", 6), (1100, 128, "f32", 4),
-], ids=["bf16_T250", "bf16_T700", "bf16_T1501", "f32_T300", "bf16_E6", "f32_T1100_E4"])
+    (300, 128, "f32", 8), (90, 256, "bf16", 6), (1100, 128, "f32", 4), (1100, 256, "bf16", 6),
+    (2053, 256, "bf16", 8),
+], ids=["bf16_T250", "bf16_T700", "bf16_T1501", "f32_T300", "bf16_E6", "f32_T1100_E4",
+        "bf16_T1100_E6", "bf16_T2053"])
 def test_block_staged_equals_one_call(moe, T, d, dtype, E):
     """moe_rmsnorm + the staged layer + moe_combine_residual reproduce
     moe_block_forward bit for bit (routing, weights and y; bf16 output too).
-    The one call normalises inside the router's kernel; T spans its 1 and 2
-    tokens per workgroup and an odd count in the last workgroup."""
+    Below 2048 tokens (and for other than 8 bf16 experts) the one call normalises
+    inside the router's kernel, from there on it runs the norm and the 8-token
+    router as the staged calls do; T spans 1, 2 and 8 tokens per workgroup and an
+    odd count in the last workgroup."""
     std = {} if dtype == "bf16" else dict(w13_std="fan_in_d", w2_std="fan_in_h")
     cfg = mi.Config("bs", T=T, d=d, h=512, E=E, dtype=dtype, wg_std="fan_in_d", **std)
     inp = mi.make_inputs(cfg, seed=14)
