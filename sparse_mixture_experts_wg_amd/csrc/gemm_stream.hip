@@ -217,8 +217,8 @@ __device__ __forceinline__ void stream_rows(const uint16_t *__restrict__ X,
       if constexpr (NMAT == 2) {
         const f32x4 gv = acc[nt][mi], uv = acc[NT + nt][mi];
         uint2 q;
-        q.x = f32_to_bf16_bits(silu(gv[0]) * uv[0]) | (f32_to_bf16_bits(silu(gv[1]) * uv[1]) << 16);
-        q.y = f32_to_bf16_bits(silu(gv[2]) * uv[2]) | (f32_to_bf16_bits(silu(gv[3]) * uv[3]) << 16);
+        q.x = pack_bf16x2(silu(gv[0]) * uv[0], silu(gv[1]) * uv[1]);
+        q.y = pack_bf16x2(silu(gv[2]) * uv[2], silu(gv[3]) * uv[3]);
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o) = q;
       } else {
         const f32x4 v = acc[nt][mi];

@@ -459,8 +459,8 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
 #pragma unroll
         for (int s = 0; s < 4; ++s) v[s] = silu(acc[f][t][s]) * acc[f + 4][t][s];
         uint2 pk;
-        pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-        pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + orow + col) = pk;
       }
     } else {
@@ -621,8 +621,8 @@ __device__ __forceinline__ void small_body(
 #pragma unroll
         for (int s = 0; s < 4; ++s) v[s] = silu(acc[0][t][4 * q + s]) * acc[1][t][4 * q + s];
         uint2 pk;
-        pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-        pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + orow + col) = pk;
       }
     } else {
