@@ -31,7 +31,7 @@
 //    fastest, so concurrently running tiles share weight tiles; the linear tile
 //    id is remapped so that each of the 8 XCDs (workgroups are dealt to XCDs
 //    round-robin) owns one contiguous range of tiles and its own L2 sees the
-//    reuse. Token rows past an expert's end read a row of zeros (g_zero_row);
+//    reuse. Token rows past a tile's end read a row of zeros (g_zero_row);
 //    their results are never stored.
 //  * Down can split the sum over h into `ksplit` parts: each part is a tile of
 //    its own writing float32 partial sums that the combine step adds in a fixed
@@ -190,13 +190,16 @@ __device__ __forceinline__ void dma16_nt(const uint16_t *g, lds_void *l) {
 }
 
 // The tile of this workgroup: expert e (rows row0 .. row0 + ne - 1), token
-// block m0, output column c0 and, with ksplit > 1 (down only), the part ks of
-// the sum over K. False when the workgroup has no tile.
+// rows m0 .. lim - 1 of it, output column c0 and, with ksplit > 1 (down only),
+// the part ks of the sum over K. False when the workgroup has no tile.
 struct Tile {
-  int e, row0, ne, m0, c0, ks;
+  int e, row0, ne, m0, lim, c0, ks;
 };
 
-template <int BT, int kCols>
+// EVEN: an expert's ceil(ne / BT) token tiles split its rows evenly (tile m holds
+// rows m ne / mtiles .. (m + 1) ne / mtiles - 1, all within one row of each other)
+// instead of BT rows each and the rest in the last.
+template <int BT, int kCols, bool EVEN = false>
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int N,
                                           int ksplit, Tile &tl) {
   const int ct = (N + kCols - 1) / kCols;
@@ -220,14 +223,23 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
   tl.e = e;
   tl.row0 = row0;
   tl.ne = ne;
-  tl.m0 = (L % mtiles) * BT;
+  const int m = L % mtiles;
+  if constexpr (EVEN) {
+    tl.m0 = int(int64_t(m) * ne / mtiles);
+    tl.lim = int(int64_t(m + 1) * ne / mtiles);
+  } else {
+    tl.m0 = m * BT;
+    tl.lim = min(ne, tl.m0 + BT);
+  }
   tl.c0 = (L / mtiles) * kCols;
   return true;
 }
 
 // ---- BT = 256: the 16 x 16 x 32 body ---------------------------------------------
-// 8 wavefronts (2 per SIMD) in a 2 x 4 grid; each owns 128 weight rows x 64 tokens
-// as 8 x 4 accumulators of v_mfma_f32_16x16x32_bf16 (A: lane holds weight row
+// 8 wavefronts (2 per SIMD) in a 2 x 4 grid; each owns 128 weight rows x 4 token
+// fragments of 16 (every fourth fragment of the tile, so that a tile of fewer rows
+// leaves every wavefront about the same work) as 8 x 4 accumulators of
+// v_mfma_f32_16x16x32_bf16 (A: lane holds weight row
 // lane & 15 and k 8 (lane >> 4) + 0..7 of a 32-wide k-step; B the same for a token;
 // D: token lane & 15, weight rows 4 (lane >> 4) + 0..3). A 64-wide k-block is two
 // 32-wide k-steps. On MI355X this shape runs the same tile 4-6% faster than the
@@ -235,20 +247,20 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
 // and gives the same sums to the bit: both add the products of each 16-wide half of
 // a 32-wide k-step into the accumulator in the same order.
 //
-// Fragment f (weight rows 16 f .. 16 f + 15 of the wavefront's block, or tokens
-// 16 t ..), k-step kk: logical chunk 4 kk + (lane >> 4) of row 16 f + (lane & 15)
-// sits at physical chunk (lane >> 4) ^ swz(lane & 15) ^ 4 kk ^ (f & 1) kOddXor / 16,
-// so every read address is lane_base ^ (64 kk | (f & 1) kOddXor) + 2048 f. The empty
+// Weight fragment f (rows 16 f .. 16 f + 15 of the wavefront's block), k-step kk:
+// logical chunk 4 kk + (lane >> 4) of row 16 f + (lane & 15) sits at physical chunk
+// (lane >> 4) ^ swz(lane & 15) ^ 4 kk ^ (f & 1) kOddXor / 16, so every read address
+// is lane_base ^ (64 kk | (f & 1) kOddXor) + 2048 f; token fragment t (tile rows
+// 16 (4 t + wc) ..) is lane_base ^ 64 kk + 8192 t, its parity fixed by wc. The empty
 // asm hands each k-step a fresh copy of the lane base, so that the compiler does not
 // keep one address register per slot, k-step and parity live across the loop.
 #define M16_READ_B(SX, KK, BUF)                                                            \
   {                                                                                        \
     uint32_t lb_ = laneB;                                                                  \
     asm volatile("" : "+v"(lb_));                                                          \
-    const char *p0_ = reinterpret_cast<const char *>(SX) + (lb_ ^ (64 * (KK)));            \
-    const char *p1_ = reinterpret_cast<const char *>(SX) + (lb_ ^ (64 * (KK) + kOddXor));  \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) fb[BUF][t] =                             \
-        *reinterpret_cast<const bf16x8 *>(((t & 1) ? p1_ : p0_) + t * 2048);               \
+    const char *p_ = reinterpret_cast<const char *>(SX) + (lb_ ^ (64 * (KK)));             \
+    _Pragma("unroll") for (int t = 0; t < NT; ++t) fb[BUF][t] =                            \
+        *reinterpret_cast<const bf16x8 *>(p_ + t * 8192);                                  \
   }
 #define M16_READ_A(SW, KK, BUF, H)                                                         \
   {                                                                                        \
@@ -261,7 +273,7 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
   }
 #define M16_MFMA(BUF, H)                                                                   \
   _Pragma("unroll") for (int f = 4 * (H); f < 4 * (H) + 4; ++f)                           \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                          \
+    _Pragma("unroll") for (int t = 0; t < NT; ++t)                                         \
       acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[BUF][f], fb[BUF][t], acc[f][t], \
                                                           0, 0, 0);
 // Multiply the fragments in BUF while k-step KKN of (SW, SX) is read into BUFN, in
@@ -369,7 +381,12 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 2, wc = wave & 3;
+  // wavefront w takes weight rows 128 wr .. and the token fragments wc, wc + 4, ...;
+  // with the wavefronts of a workgroup placed on the SIMDs in turn (w and w + 4 on
+  // SIMD w % 4), the two of a SIMD hold wc and wc ^ 2, whose fragment counts add up
+  // to the same on every SIMD when a tile has fewer than 16 fragments (other
+  // assignments measured the same to within 1%)
+  const int wr = wave >> 2, wc = (wave & 3) ^ (wr << 1);
 
   // ---- DMA assignment: wave w fills rows [32w, 32w+32) of both tiles, 8 rows
   // per instruction; lane p writes LDS bytes [16p, 16p+16) of the
@@ -393,20 +410,23 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
     if constexpr (GATEUP) wrow = tl.c0 + ((r >> 7) << 6) + (r & 63);
     else wrow = min(tl.c0 + r, N - 1);
     wofs[i] = (uint32_t(wrow) * uint32_t(K) + c * 8) * 2u;
-    if (r > tl.ne - 1 - tl.m0 && K <= kZeroK) {
+    if (r > tl.lim - 1 - tl.m0 && K <= kZeroK) {
       xsrc[i] = g_zero_row + c * 8;
     } else {
-      const int xr = tl.row0 + tl.m0 + min(r, tl.ne - 1 - tl.m0);
+      const int xr = tl.row0 + tl.m0 + min(r, tl.lim - 1 - tl.m0);
       xsrc[i] = X + size_t(rowmap ? rowmap[xr] : xr) * K + c * 8;
     }
   }
   const int dma_row = wave * 32;
 
   // ---- fragment read bases (bytes): row lane & 15 of the wavefront's first
-  // weight (token) fragment, physical chunk of logical chunk lane >> 4
+  // weight (token) fragment, physical chunk of logical chunk lane >> 4. Token
+  // fragment t of the wavefront is tile rows 16 (4 t + wc) .., whose rows all have
+  // the swizzle parity of wc: one base, 8 KiB (64 rows) apart.
   const uint32_t lchunk = uint32_t(((lane >> 4) ^ swz(lane & 15)) << 4);
   const uint32_t laneA = uint32_t((wr * 128 + (lane & 15)) * 128) | lchunk;
-  const uint32_t laneB = uint32_t((wc * 64 + (lane & 15)) * 128) | lchunk;
+  const uint32_t laneB = uint32_t((wc * 16 + (lane & 15)) * 128) |
+                         uint32_t(((lane >> 4) ^ swz(16 * (wc & 1) + (lane & 15))) << 4);
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -437,18 +457,34 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
   // 4 weight + 4 token copies per wavefront and k-block; the prologue waits for
   // k-block 0 with the weights of 1 and 2 and the tokens of 1 in flight
   constexpr int kStepWait = wait_vm_lgkm0(4);
-  M16_KLOOP(wait_vm(12))
+  // Matrix work only for the token fragments that hold rows: the wavefront's
+  // fragments below nf = ceil(rows / 16) (4, 3, or 2 and fewer, which take the
+  // 2-fragment loop; rows past the tile are the zero row or a repeat, their sums
+  // are not stored)
+  const int nf = (tl.lim - tl.m0 + 15) >> 4;
+  const int nt = (nf - wc + 3) >> 2;
+  if (nt >= 4) {
+    constexpr int NT = 4;
+    M16_KLOOP(wait_vm(12))
+  } else if (nt == 3) {
+    constexpr int NT = 3;
+    M16_KLOOP(wait_vm(12))
+  } else {
+    constexpr int NT = 2;
+    M16_KLOOP(wait_vm(12))
+  }
 #undef DMAW
 #undef DMAX
 
-  // ---- epilogue: lane holds token wc * 64 + 16 t + (lane & 15) and weight rows
+  // ---- epilogue: lane holds token 16 (4 t + wc) + (lane & 15) and weight rows
   // 16 f + 4 (lane >> 4) + 0..3 of the wavefront's 128; for gate-up fragments 0-3
-  // are g and 4-7 the u of the same 64 columns
+  // are g and 4-7 the u of the same 64 columns. Fragments t >= NT lie at or past
+  // the tile's end.
   const int ih = 4 * (lane >> 4);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int tok = tl.m0 + wc * 64 + t * 16 + (lane & 15);
-    if (tok >= tl.ne) continue;
+    const int tok = tl.m0 + 16 * (4 * t + wc) + (lane & 15);
+    if (tok >= tl.lim) continue;
     const size_t orow = size_t(tl.row0 + tok) * N + size_t(tl.ks) * size_t(part_stride);
     if constexpr (GATEUP) {
 #pragma unroll
@@ -672,17 +708,20 @@ __global__ __launch_bounds__(512) void tiled128_kernel(
                                 sW2, sX0, sX1);
 }
 
-// Experts of more than a few hundred rows: 256-token tiles (body256).
-// Narrowing each expert's last, partly filled tile to 64 or 128 tokens (33
-// instead of 36 full tiles' worth of matrix work at the 8x7B prefill shape)
-// was measured on MI355X, in one process, interleaved: gate-up 1.79 vs 1.81 ms
-// and down 0.95 vs 0.97 ms on the mean, no gain on the best runs, and twice
-// the HBM reads (3.1 -> 5.9 GB per gate-up launch): a narrow tail has a quarter
-// of a full tile's matrix work, runs ahead of its expert's full tiles of the
-// same column block through the k-loop and fetches the shared weight slices
-// first, and the full tiles then find them evicted from L2. Running all tails
-// after the full tiles cut that to 4.7 GB and was slower. Every tile is 256
-// tokens wide.
+// Experts of more than a few hundred rows: up to 256 tokens per tile (body256),
+// an expert's ceil(rows / 256) tiles splitting its rows evenly (an expert of 1062
+// rows: 5 tiles of 212-213 rows, 14 fragments, instead of 4 x 256 and 38), and
+// each wavefront multiplying only its fragments that hold rows. The tiles of one
+// expert and column block then run the same length and stay in step through the
+// k-loop, so that the weight slices they share are fetched once. On MI355X in one
+// process, interleaved: gate-up 1.565 -> 1.520 ms and down 0.864 -> 0.849 ms at
+// the prefill_8x7b routing (matrix work 12.5% -> 3.7% above the algorithmic), 1%
+// at skew_8x7b, 8% at a ragged routing of 2200 rows, bitwise the same outputs.
+// Narrowing only the last tile to 64 or 128 tokens was no faster and doubled the
+// HBM reads (3.1 -> 5.9 GB per gate-up launch): a narrow tail runs ahead of its
+// expert's full tiles and fetches the shared weight slices first, which the full
+// tiles then find evicted from L2; running all tails after the full tiles cut that
+// to 4.7 GB and was slower.
 template <bool GATEUP>
 __global__ __launch_bounds__(512) void tiled256_kernel(
     const uint16_t *__restrict__ X, const int32_t *__restrict__ offsets, int E,
@@ -694,7 +733,7 @@ __global__ __launch_bounds__(512) void tiled256_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t sX0[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX1[256 * 64];
   Tile tl;
-  if (!find_tile<256, GATEUP ? 128 : 256>(offsets, E, N, ksplit, tl)) return;
+  if (!find_tile<256, GATEUP ? 128 : 256, true>(offsets, E, N, ksplit, tl)) return;
   body256<GATEUP>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1, sW2, sX0, sX1);
 }
 

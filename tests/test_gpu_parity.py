@@ -488,6 +488,12 @@ EXPERT_CASES = [
     ("tiled_tail_fragments", "tiled", 600, 256, 512, [65, 112, 113, 64, 16, 17, 48, 49], 0, 1),
     ("tiled_tail_fragments_p4", "tiled", 600, 256, 512, [65, 112, 113, 64, 16, 17, 48, 49], 1,
      4),
+    # an expert's 256-token tiles split its rows evenly: 5 tiles of 212-213 rows (14
+    # fragments), 208-209 (13), single tiles of 224 and 225 rows (14 and 15 fragments)
+    ("tiled_even_split", "tiled", 2000, 256, 512, [1062, 1043, 1026, 208, 209, 224, 225, 0],
+     0, 1),
+    ("tiled_even_split_p4", "tiled", 2000, 256, 512, [1062, 1043, 1026, 208, 209, 224, 225, 0],
+     1, 4),
 ]
 
 
