@@ -95,7 +95,9 @@ int64_t moe_capacity_rows(int64_t T, int32_t K, int32_t E, int64_t cf_num, int64
  *   split the sum over h into moe_down_parts(p) float32 partial sums, stored one
  *   after another in o_perm ([parts, S, d]), and moe_combine (given the same
  *   flags) adds them in part order before weighting. With few row tiles per
- *   expert this keeps every compute unit busy in the down projection. */
+ *   expert this keeps every compute unit busy in the down projection. The parts
+ *   cover consecutive ranges of h, not necessarily of equal length (the library
+ *   sizes them from the routing); only their sum is defined. */
 #define MOE_FLAG_DOWN_PARTIALS 1
 
 typedef struct {

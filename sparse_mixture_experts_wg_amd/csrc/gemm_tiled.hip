@@ -191,27 +191,59 @@ __device__ __forceinline__ void dma16_nt(const uint16_t *g, lds_void *l) {
 
 // The tile of this workgroup: expert e (rows row0 .. row0 + ne - 1), token
 // rows m0 .. lim - 1 of it, output column c0 and, with ksplit > 1 (down only),
-// the part ks of the sum over K. False when the workgroup has no tile.
+// the part ks of the sum over K: 64-wide k-blocks kb0 .. kb0 + nkp - 1. False
+// when the workgroup has no tile.
 struct Tile {
-  int e, row0, ne, m0, lim, c0, ks;
+  int e, row0, ne, m0, lim, c0, ks, kb0, nkp;
 };
+
+constexpr int kCUsPerXCD = 32;  // MI355X: 256 compute units in 8 XCDs
+
+// Where part 0 of a 2-way split of nkt k-blocks ends, for g tiles per part on each
+// XCD. The workgroups of an XCD run part 0 of its g tiles first, then part 1, one
+// per compute unit at a time. With g = q C + r (C compute units, 0 < r, q >= 1), an
+// even split leaves C - r units idle through the last round; a longer part 0
+// (q or q + 1 of them per unit) and a shorter part 1 that fills the units that
+// finished part 0 a round early end together when part 0 holds the fraction
+// g / (g + C - r) of the k-blocks (prefill_8x7b down: g = 72, C = 32, 168 of 224
+// k-blocks). Rounded to an even count, clamped to [nkt / 2, nkt - 2].
+__device__ __forceinline__ int split_point(int g, int nkt) {
+  const int C = kCUsPerXCD, q = g / C, r = g % C;
+  if (q == 0 || r == 0) return nkt / 2;
+  const int64_t den = int64_t(g + C - r);
+  const int a = int((int64_t(nkt) * g + den) / (2 * den)) * 2;  // nearest even
+  return max(nkt / 2, min(nkt - 2, a));
+}
 
 // EVEN: an expert's ceil(ne / BT) token tiles split its rows evenly (tile m holds
 // rows m ne / mtiles .. (m + 1) ne / mtiles - 1, all within one row of each other)
 // instead of BT rows each and the rest in the last.
-template <int BT, int kCols, bool EVEN = false>
+// The tiles of a part are ordered (expert, column block, token block); each XCD
+// (workgroups are dealt to the XCDs in turn) takes one contiguous range of g of
+// them, all parts of it, part-major, so that the tiles sharing a weight or token
+// slice run on one XCD at one time.
+template <int BT, int kCols, bool EVEN = false, bool UNEVEN = true>
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int N,
-                                          int ksplit, Tile &tl) {
+                                          int K, int ksplit, Tile &tl) {
   const int ct = (N + kCols - 1) / kCols;
   int total = 0;
   for (int q = 0; q < E; ++q) total += ct * ((offsets[q + 1] - offsets[q] + BT - 1) / BT);
-  const int g8 = (total * ksplit + kXCD - 1) / kXCD;
+  const int g = (total + kXCD - 1) / kXCD;
   const int b = blockIdx.x;
-  if (b >= g8 * kXCD) return false;
-  int L = (b % kXCD) * g8 + b / kXCD;
-  if (L >= total * ksplit) return false;
-  tl.ks = L / total;
-  L -= tl.ks * total;
+  const int i = b / kXCD;
+  if (i >= g * ksplit) return false;
+  tl.ks = i / g;
+  int L = (b % kXCD) * g + i % g;
+  if (L >= total) return false;
+  const int nkt = K / 64;
+  if (ksplit == 2 && UNEVEN) {
+    const int a = split_point(g, nkt);
+    tl.kb0 = tl.ks ? a : 0;
+    tl.nkp = tl.ks ? nkt - a : a;
+  } else {
+    tl.nkp = nkt / ksplit;
+    tl.kb0 = tl.ks * tl.nkp;
+  }
   int e = 0, row0 = 0, ne = 0, mtiles = 0;
   for (; e < E; ++e) {
     row0 = offsets[e];
@@ -437,8 +469,8 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
       for (int i = 0; i < 4; ++i) acc[f][t][i] = 0.f;
   bf16x8 fa[2][8], fb[2][4];
 
-  const int nk = K / 64 / ksplit;  // k-blocks of this part (an even count)
-  const int kb0 = tl.ks * nk;
+  const int nk = tl.nkp;  // k-blocks of this part (an even count)
+  const int kb0 = tl.kb0;
 
 #define DMAW(SW, KB)                                                                       \
   {                                                                                        \
@@ -591,8 +623,8 @@ __device__ __forceinline__ void small_body(
       for (int i = 0; i < 16; ++i) acc[f][t][i] = 0.f;
   bf16x8 fa[2][FA], fb[2][FB];
 
-  const int nk = K / 64 / ksplit;  // k-blocks of this part (an even count)
-  const int kb0 = ks * nk;
+  const int nk = tl.nkp;  // k-blocks of this part (an even count)
+  const int kb0 = tl.kb0;
 
 #define DMAW(SW, KB)                                                                       \
   {                                                                                        \
@@ -687,7 +719,7 @@ __global__ __launch_bounds__(512) void tiled64_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t sX0[64 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX1[64 * 64];
   Tile tl;
-  if (!find_tile<64, GATEUP ? 128 : 256>(offsets, E, N, ksplit, tl)) return;
+  if (!find_tile<64, GATEUP ? 128 : 256>(offsets, E, N, K, ksplit, tl)) return;
   small_body<GATEUP, 64, false>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1,
                                 nullptr, sX0, sX1);
 }
@@ -703,7 +735,7 @@ __global__ __launch_bounds__(512) void tiled128_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t sX0[128 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX1[128 * 64];
   Tile tl;
-  if (!find_tile<128, GATEUP ? 128 : 256>(offsets, E, N, ksplit, tl)) return;
+  if (!find_tile<128, GATEUP ? 128 : 256>(offsets, E, N, K, ksplit, tl)) return;
   small_body<GATEUP, 128, true>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1,
                                 sW2, sX0, sX1);
 }
@@ -733,15 +765,16 @@ __global__ __launch_bounds__(512) void tiled256_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t sX0[256 * 64];
   __shared__ __attribute__((aligned(1024))) uint16_t sX1[256 * 64];
   Tile tl;
-  if (!find_tile<256, GATEUP ? 128 : 256, true>(offsets, E, N, ksplit, tl)) return;
+  if (!find_tile<256, GATEUP ? 128 : 256, true>(offsets, E, N, K, ksplit, tl)) return;
   body256<GATEUP>(tl, X, Wa, Wb, out, N, K, ksplit, part_stride, rowmap, sW0, sW1, sW2, sX0, sX1);
 }
 
 // Upper bound of the tile count for any split of S rows over E experts.
+// (every XCD gets the same count of tiles per part: find_tile's g of them)
 inline unsigned tiled_grid(int64_t S, int E, int N, int cols, int bt, int ksplit) {
   const int64_t ct = (N + cols - 1) / cols;
-  const int64_t tiles = ksplit * ct * ((S + bt - 1) / bt + E);
-  return unsigned((tiles + kXCD - 1) / kXCD * kXCD);
+  const int64_t tiles = ct * ((S + bt - 1) / bt + E);
+  return unsigned((tiles + kXCD - 1) / kXCD * kXCD * ksplit);
 }
 
 template <bool GATEUP>

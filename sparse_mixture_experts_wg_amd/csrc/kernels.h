@@ -88,7 +88,9 @@ hipError_t launch_tiled_gate_up(const void *x_perm, const int32_t *rowmap, const
                                 const void *w1, const void *w3, void *act, int E, int64_t S,
                                 int d, int h, int bt, hipStream_t s);
 // parts (1, 2 or 4; needs h % (128 * parts) == 0): partial sums over h, part q
-// at o_perm + q * S * d.
+// at o_perm + q * S * d. Equal ranges of h, except that with 2 parts part 0 may take
+// more of it (chosen on the device from the tile count, so that the last round of
+// workgroups is full).
 hipError_t launch_tiled_down(const void *act, const int32_t *offsets, const void *w2,
                              float *o_perm, int E, int64_t S, int d, int h, int bt, int parts,
                              hipStream_t s);
