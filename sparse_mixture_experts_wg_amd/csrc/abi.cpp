@@ -97,9 +97,16 @@ moe_status check_problem(const moe_problem *p) {
     return fail(MOE_ERR_UNSUPPORTED,
                 "T=%lld d=%lld: T * ceil(d / 1024) must stay below 2^24 (grid size)",
                 (long long)p->T, (long long)p->d);
-  const int64_t tiles_gu = (p->h / 128) * ((S + gate_up_tile(p) - 1) / gate_up_tile(p) + p->E);
-  const int64_t tiles_dn = 4 * ((p->d + 255) / 256) * ((S + down_tile(p) - 1) / down_tile(p) + p->E);
-  if ((std::max(tiles_gu, tiles_dn) + 7) / 8 * 8 * 512 > kMaxItems)
+  // workgroups of the tiled launches (as the kernels' grid: 8 XCDs; for 256-token
+  // tiles every XCD may get ceil(column blocks / 8) blocks of every token block)
+  auto tiled_wgs = [&](int64_t ct, int64_t bt, int64_t parts) {
+    const int64_t mt = (S + bt - 1) / bt + p->E;
+    const int64_t per_xcd = bt == 256 ? (ct + 7) / 8 * mt : (ct * mt + 7) / 8;
+    return per_xcd * 8 * parts;
+  };
+  const int64_t wgs_gu = tiled_wgs((p->h + 127) / 128, gate_up_tile(p), 1);
+  const int64_t wgs_dn = tiled_wgs((p->d + 255) / 256, down_tile(p), 4);
+  if (std::max(wgs_gu, wgs_dn) * 512 > kMaxItems)
     return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch (tiled grid size)");
   // stream grid: S / 32 row groups in the z dimension
   if (p->dtype == MOE_BF16 && resolve(p) == MOE_PATH_STREAM && (S + 31) / 32 >= (int64_t(1) << 16))

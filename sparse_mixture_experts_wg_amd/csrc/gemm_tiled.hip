@@ -27,12 +27,13 @@
 //    columns, interleaved so that every wavefront holds g and u of the same
 //    columns and applies silu(g) * u in registers; the result is rounded once to
 //    bf16. Down: 256 W2 rows = 256 output columns, float32 out.
-//  * Tiles are ordered (expert, column block, token block) with the token block
-//    fastest, so concurrently running tiles share weight tiles; the linear tile
-//    id is remapped so that each of the 8 XCDs (workgroups are dealt to XCDs
-//    round-robin) owns one contiguous range of tiles and its own L2 sees the
-//    reuse. Token rows past a tile's end read a row of zeros (g_zero_row);
-//    their results are never stored.
+//  * Each of the 8 XCDs (workgroups are dealt to XCDs in turn) runs its tiles
+//    with the token block fastest, so concurrently running tiles share weight
+//    tiles in its own L2: the 256-token tiles take the (expert, column block)
+//    groups round-robin over the XCDs, the narrower ones one contiguous range of
+//    the (expert, column block, token block) order per XCD (see find_tile).
+//    Token rows past a tile's end read a row of zeros (g_zero_row); their
+//    results are never stored.
 //  * Down can split the sum over h into `ksplit` parts: each part is a tile of
 //    its own writing float32 partial sums that the combine step adds in a fixed
 //    order, so that the last round of tiles fills the GPU.
@@ -215,26 +216,44 @@ __device__ __forceinline__ int split_point(int g, int nkt) {
   return max(nkt / 2, min(nkt - 2, a));
 }
 
+// Column blocks c of expert e that XCD x takes under the round-robin order below:
+// c = first, first + 8, ... < ct, where (e ct + c) % 8 == x.
+__device__ __forceinline__ int rr_first(int e, int x, int ct) {
+  return ((x - e * ct) % kXCD + kXCD) % kXCD;
+}
+__device__ __forceinline__ int rr_groups(int e, int x, int ct) {
+  const int c0 = rr_first(e, x, ct);
+  return c0 < ct ? (ct - 1 - c0) / kXCD + 1 : 0;
+}
+
 // EVEN: an expert's ceil(ne / BT) token tiles split its rows evenly (tile m holds
 // rows m ne / mtiles .. (m + 1) ne / mtiles - 1, all within one row of each other)
-// instead of BT rows each and the rest in the last.
-// The tiles of a part are ordered (expert, column block, token block); each XCD
-// (workgroups are dealt to the XCDs in turn) takes one contiguous range of g of
-// them, all parts of it, part-major, so that the tiles sharing a weight or token
-// slice run on one XCD at one time.
+// instead of BT rows each and the rest in the last; the tiles of different experts
+// then differ in length, so the XCDs (workgroups are dealt to them in turn) take the
+// (expert, column block) groups round-robin: XCD x runs the groups e ct + c = x mod 8,
+// each with all its token blocks one after another, expert by expert, so that every
+// XCD gets the same share of every expert (prefill_8x7b: 14 of each expert's 112
+// gate-up column blocks) and the token blocks sharing a weight slice run on one XCD
+// at one time. Otherwise the tiles of a part are ordered (expert, column block, token
+// block) and each XCD takes one contiguous range of g of them. Either way an XCD runs
+// all parts of its tiles, part-major.
 template <int BT, int kCols, bool EVEN = false, bool UNEVEN = true>
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int N,
                                           int K, int ksplit, Tile &tl) {
   const int ct = (N + kCols - 1) / kCols;
-  int total = 0;
-  for (int q = 0; q < E; ++q) total += ct * ((offsets[q + 1] - offsets[q] + BT - 1) / BT);
-  const int g = (total + kXCD - 1) / kXCD;
-  const int b = blockIdx.x;
-  const int i = b / kXCD;
+  const int x = blockIdx.x % kXCD, i = blockIdx.x / kXCD;
+  int g = 0;      // tiles per part on this XCD
+  int total = 0;  // tiles per part (contiguous order)
+  if constexpr (EVEN) {
+    for (int q = 0; q < E; ++q)
+      g += rr_groups(q, x, ct) * ((offsets[q + 1] - offsets[q] + BT - 1) / BT);
+  } else {
+    for (int q = 0; q < E; ++q) total += ct * ((offsets[q + 1] - offsets[q] + BT - 1) / BT);
+    g = (total + kXCD - 1) / kXCD;
+  }
   if (i >= g * ksplit) return false;
   tl.ks = i / g;
-  int L = (b % kXCD) * g + i % g;
-  if (L >= total) return false;
+  int L = i % g;
   const int nkt = K / 64;
   if (ksplit == 2 && UNEVEN) {
     const int a = split_point(g, nkt);
@@ -245,12 +264,29 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
     tl.kb0 = tl.ks * tl.nkp;
   }
   int e = 0, row0 = 0, ne = 0, mtiles = 0;
-  for (; e < E; ++e) {
-    row0 = offsets[e];
-    ne = offsets[e + 1] - row0;
-    mtiles = (ne + BT - 1) / BT;
-    if (L < ct * mtiles) break;
-    L -= ct * mtiles;
+  if constexpr (EVEN) {
+    int ng = 0;
+    for (; e < E; ++e) {
+      row0 = offsets[e];
+      ne = offsets[e + 1] - row0;
+      mtiles = (ne + BT - 1) / BT;
+      ng = rr_groups(e, x, ct);
+      if (L < ng * mtiles) break;
+      L -= ng * mtiles;
+    }
+    // L < g, so some expert holds it: L = group index * mtiles + token block
+    tl.c0 = (rr_first(e, x, ct) + kXCD * (L / mtiles)) * kCols;
+  } else {
+    L += x * g;
+    if (L >= total) return false;
+    for (; e < E; ++e) {
+      row0 = offsets[e];
+      ne = offsets[e + 1] - row0;
+      mtiles = (ne + BT - 1) / BT;
+      if (L < ct * mtiles) break;
+      L -= ct * mtiles;
+    }
+    tl.c0 = (L / mtiles) * kCols;
   }
   tl.e = e;
   tl.row0 = row0;
@@ -263,7 +299,6 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
     tl.m0 = m * BT;
     tl.lim = min(ne, tl.m0 + BT);
   }
-  tl.c0 = (L / mtiles) * kCols;
   return true;
 }
 
@@ -770,11 +805,14 @@ __global__ __launch_bounds__(512) void tiled256_kernel(
 }
 
 // Upper bound of the tile count for any split of S rows over E experts.
-// (every XCD gets the same count of tiles per part: find_tile's g of them)
+// (per part, an XCD gets at most ceil(tiles / 8) tiles in the contiguous order and
+// at most ceil(ct / 8) column blocks of every token block in the round-robin order
+// of the 256-token tiles)
 inline unsigned tiled_grid(int64_t S, int E, int N, int cols, int bt, int ksplit) {
   const int64_t ct = (N + cols - 1) / cols;
-  const int64_t tiles = ct * ((S + bt - 1) / bt + E);
-  return unsigned((tiles + kXCD - 1) / kXCD * kXCD * ksplit);
+  const int64_t mt = (S + bt - 1) / bt + E;  // token blocks, at most
+  const int64_t per_xcd = bt == 256 ? (ct + kXCD - 1) / kXCD * mt : (ct * mt + kXCD - 1) / kXCD;
+  return unsigned(per_xcd * kXCD * ksplit);
 }
 
 template <bool GATEUP>
