@@ -71,7 +71,7 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 } moe_
  * for d <= 4096, MOE_STREAM_MAX_T_WIDE for larger d (batch-size sweeps on
  * MI355X at the Mixtral 8x7B shape, d = 4096, h = 14336, and the 8x22B shape,
  * d = 6144, h = 16384). */
-#define MOE_STREAM_MAX_T 72
+#define MOE_STREAM_MAX_T 96
 #define MOE_STREAM_MAX_T_WIDE 32
 
 /* moe_problem.capacity (the capacity variant; the pages name the capacity

@@ -91,9 +91,9 @@ def test_bad_dtype_and_flags():
 
 def test_path_resolution():
     # the automatic switch point comes from a batch-size sweep on MI355X (bench.py --sweep)
-    assert moe.resolve_path(_p(T=72)) == binding.PATH_STREAM
-    assert moe.resolve_path(_p(T=73)) == binding.PATH_TILED
-    assert moe.resolve_path(_p(T=72, d=4096)) == binding.PATH_STREAM
+    assert moe.resolve_path(_p(T=96)) == binding.PATH_STREAM
+    assert moe.resolve_path(_p(T=97)) == binding.PATH_TILED
+    assert moe.resolve_path(_p(T=96, d=4096)) == binding.PATH_STREAM
     # wider models switch earlier (the 8x22B shape, d = 6144)
     assert moe.resolve_path(_p(T=32, d=6144, h=16384)) == binding.PATH_STREAM
     assert moe.resolve_path(_p(T=33, d=6144, h=16384)) == binding.PATH_TILED

@@ -83,8 +83,8 @@ SMALL = [
     # about 1024 rows per expert, every token compared
     ("bf16_tiled_T4096", mi.Config("s1b", T=4096, d=256, h=512, wg_std="fan_in_d"), "auto"),
     ("bf16_tiled_T65", mi.Config("s2", T=65, d=384, h=256, wg_std="fan_in_d"), "tiled"),
-    ("bf16_auto_T73_tiled", mi.Config("s2b", T=73, d=384, h=256, wg_std="fan_in_d"), "auto"),
-    ("bf16_auto_T72_stream", mi.Config("s2c", T=72, d=256, h=384, wg_std="fan_in_d"), "auto"),
+    ("bf16_auto_T97_tiled", mi.Config("s2b", T=97, d=384, h=256, wg_std="fan_in_d"), "auto"),
+    ("bf16_auto_T96_stream", mi.Config("s2c", T=96, d=256, h=384, wg_std="fan_in_d"), "auto"),
     ("bf16_tiled_T193", mi.Config("s2d", T=193, d=384, h=256, wg_std="fan_in_d"), "tiled"),
     # about 113 rows per expert: still 128-token tiles (n + sqrt(n) <= 128)
     ("bf16_tiled128_T450", mi.Config("s2e", T=450, d=256, h=512, wg_std="fan_in_d"), "auto"),
