@@ -102,6 +102,13 @@ SMALL = [
      "auto"),
     ("bf16_E2_K2_stream", mi.Config("s11", T=20, d=256, h=256, E=2, K=2, wg_std="fan_in_d"),
      "auto"),
+    # 256-token tiles with fewer column blocks than XCDs (d = 384: 2 down blocks; h = 640:
+    # 5 gate-up blocks) and 6 experts of about 667 rows (3 even tiles each); K = 1 with
+    # about 375 rows per expert (2 tiles of 12 fragments)
+    ("bf16_E6_T2000_tiled", mi.Config("s14", T=2000, d=384, h=640, E=6, K=2,
+                                      wg_std="fan_in_d"), "auto"),
+    ("bf16_K1_T3000_tiled", mi.Config("s15", T=3000, d=256, h=384, E=8, K=1,
+                                      wg_std="fan_in_d"), "auto"),
     ("f32_ragged", mi.Config("s9", T=333, d=128, h=384, dtype="f32", w13_std="fan_in_d",
                              w2_std="fan_in_h"), "auto"),
     # extreme widths: h above the 65536-element zero row (the down projection's padding
