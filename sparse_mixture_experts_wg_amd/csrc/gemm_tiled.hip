@@ -455,13 +455,21 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
   // assignments measured the same to within 1%)
   const int wr = wave >> 2, wc = (wave & 3) ^ (wr << 1);
 
-  // ---- DMA assignment: wave w fills rows [32w, 32w+32) of both tiles, 8 rows
-  // per instruction; lane p writes LDS bytes [16p, 16p+16) of the
-  // instruction's kilobyte: row 8i + p/8, physical chunk p%8 = logical chunk ^
-  // swz(row). Gate-up weight rows: 64 W1 rows, the W3 rows of the same
-  // columns, the next 64 W1 rows, their W3 rows. Weight offsets are bytes from
-  // the expert's matrix (h d < 2^31, so they fit 32 bits), so the copies take a
-  // uniform base and a 32-bit per-lane offset.
+  // ---- DMA assignment, 8 rows per instruction; lane p writes LDS bytes
+  // [16p, 16p+16) of the instruction's kilobyte: row 8i + p/8 of its 8, physical
+  // chunk p%8 = logical chunk ^ swz(row). Weights: wave w fills rows [32w, 32w+32).
+  // Gate-up weight rows: 64 W1 rows, the W3 rows of the same columns, the next 64
+  // W1 rows, their W3 rows. Weight offsets are bytes from the expert's matrix
+  // (h d < 2^31, so they fit 32 bits), so the copies take a uniform base and a
+  // 32-bit per-lane offset. Tokens: wave (wr, wc) fills the fragments wc + 8 wr and
+  // wc + 8 wr + 4 (two instructions each), so the wavefront with wr = 0 copies the
+  // first two fragments its column pair multiplies and the one with wr = 1 the
+  // third and fourth. A tile whose column pair multiplies only 3 or 2 fragments
+  // then leaves out the copies of the others: 4-6 of the 32 token copies per
+  // k-block at prefill_8x7b (13-14 fragments of rows), 14 at T = 1024 (9), which
+  // measured bitwise the same and 1% (prefill_8x7b), 10-11% (T = 1024 and a
+  // ragged routing of 2200 rows) faster on the gate-up, up to 2% on the down
+  // projection, against every wavefront copying 32 consecutive token rows.
   const size_t mat_elems = size_t(N) * K;
   const uint16_t *wmat = Wa + size_t(tl.e) * mat_elems;
   if (GATEUP && ((wave >> 1) & 1)) wmat = Wb + size_t(tl.e) * mat_elems;
@@ -477,14 +485,18 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
     if constexpr (GATEUP) wrow = tl.c0 + ((r >> 7) << 6) + (r & 63);
     else wrow = min(tl.c0 + r, N - 1);
     wofs[i] = (uint32_t(wrow) * uint32_t(K) + c * 8) * 2u;
-    if (r > tl.lim - 1 - tl.m0 && K <= kZeroK) {
-      xsrc[i] = g_zero_row + c * 8;
+    const int rx = 16 * (wc + 8 * wr + 4 * (i >> 1)) + 8 * (i & 1) + (lane >> 3);
+    const int cx = (lane & 7) ^ swz(rx);
+    if (rx > tl.lim - 1 - tl.m0 && K <= kZeroK) {
+      xsrc[i] = g_zero_row + cx * 8;
     } else {
-      const int xr = tl.row0 + tl.m0 + min(r, tl.lim - 1 - tl.m0);
-      xsrc[i] = X + size_t(rowmap ? rowmap[xr] : xr) * K + c * 8;
+      const int xr = tl.row0 + tl.m0 + min(rx, tl.lim - 1 - tl.m0);
+      xsrc[i] = X + size_t(rowmap ? rowmap[xr] : xr) * K + cx * 8;
     }
   }
   const int dma_row = wave * 32;
+  // LDS row of token copy i: dma_xrow + 64 (i >> 1) + 8 (i & 1)
+  const int dma_xrow = 16 * (wc + 8 * wr);
 
   // ---- fragment read bases (bytes): row lane & 15 of the wavefront's first
   // weight (token) fragment, physical chunk of logical chunk lane >> 4. Token
@@ -515,14 +527,18 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
                 reinterpret_cast<const char *>(wmat + k0) + wofs[i]),                       \
             (lds_void *)(SW + (dma_row + i * 8) * 64));                                      \
   }
+// NX of the 4 token copies: the fragments the loop multiplies
 #define DMAX(SX, KB)                                                                       \
   {                                                                                        \
     const uint32_t k0 = uint32_t((kb0 + min(KB, nk - 1)) * 64);                            \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
-      dma16(xsrc[i] + k0, (lds_void *)(SX + (dma_row + i * 8) * 64));                      \
+    _Pragma("unroll") for (int i = 0; i < NX; ++i)                                         \
+      dma16(xsrc[i] + k0,                                                                  \
+            (lds_void *)(SX + (dma_xrow + 64 * (i >> 1) + 8 * (i & 1)) * 64));             \
   }
-  // 4 weight + 4 token copies per wavefront and k-block; the prologue waits for
-  // k-block 0 with the weights of 1 and 2 and the tokens of 1 in flight
+  // 4 weight + NX token copies per wavefront and k-block, the weights issued last;
+  // the prologue waits for k-block 0 with the weights of 1 and 2 and the tokens of
+  // 1 in flight (8 + NX copies), each step for all but the last 4 (the weights of
+  // KB + 3)
   constexpr int kStepWait = wait_vm_lgkm0(4);
   // Matrix work only for the token fragments that hold rows: the wavefront's
   // fragments below nf = ceil(rows / 16) (4, 3, or 2 and fewer, which take the
@@ -530,15 +546,27 @@ __device__ __forceinline__ void body256(const Tile &tl, const uint16_t *__restri
   // are not stored)
   const int nf = (tl.lim - tl.m0 + 15) >> 4;
   const int nt = (nf - wc + 3) >> 2;
+  // (the wavefront with wr = 1 copies fragments wc + 8 and wc + 12: both for 4,
+  // the first for 3, none for 2)
   if (nt >= 4) {
-    constexpr int NT = 4;
-    M16_KLOOP(wait_vm(12))
+    constexpr int NT = 4, NX = 4;
+    M16_KLOOP(wait_vm(8 + NX))
   } else if (nt == 3) {
-    constexpr int NT = 3;
-    M16_KLOOP(wait_vm(12))
+    if (wr == 0) {
+      constexpr int NT = 3, NX = 4;
+      M16_KLOOP(wait_vm(8 + NX))
+    } else {
+      constexpr int NT = 3, NX = 2;
+      M16_KLOOP(wait_vm(8 + NX))
+    }
   } else {
-    constexpr int NT = 2;
-    M16_KLOOP(wait_vm(12))
+    if (wr == 0) {
+      constexpr int NT = 2, NX = 4;
+      M16_KLOOP(wait_vm(8 + NX))
+    } else {
+      constexpr int NT = 2, NX = 0;
+      M16_KLOOP(wait_vm(8 + NX))
+    }
   }
 #undef DMAW
 #undef DMAX
