@@ -635,7 +635,7 @@ __device__ __forceinline__ void small_body(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
 
-  // ---- DMA assignment as in tiled_kernel: wave w fills weight rows
+  // ---- DMA assignment (8 rows per instruction, as in body256): wave w fills weight rows
   // [32w, 32w+32) (for gate-up: W1 rows if w is even, else the W3 rows of the
   // same 32 columns) and token rows [w*BT/8, (w+1)*BT/8).
   const size_t mat_elems = size_t(N) * K;
@@ -736,7 +736,8 @@ __device__ __forceinline__ void small_body(
 #undef DMAW
 #undef DMAX
 
-  // ---- epilogue (fragment layout as in tiled_kernel)
+  // ---- epilogue: 32 x 32 accumulator layout, lane holds token (lane & 31) of its
+  // 32-token column and weight rows 8 q + 4 (lane >> 5) + 0..3 of each 32-row fragment
   const int ih = 4 * (lane >> 5);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {

@@ -501,6 +501,13 @@ EXPERT_CASES = [
      0, 1),
     ("tiled_even_split_p4", "tiled", 2000, 256, 512, [1062, 1043, 1026, 208, 209, 224, 225, 0],
      1, 4),
+    # tiles of 1, 2, 9, 12, 13 and 16 fragments, two of 9 (262 rows) and three of 11
+    # (513 rows) in one launch: every wavefront loop of the 256-token tile, with all,
+    # half or none of a wavefront's token copies
+    ("tiled_fragment_counts", "tiled", 2000, 256, 512, [1, 17, 129, 180, 200, 250, 262, 513],
+     0, 1),
+    ("tiled_fragment_counts_p4", "tiled", 2000, 256, 512,
+     [1, 17, 129, 180, 200, 250, 262, 513], 1, 4),
 ]
 
 
