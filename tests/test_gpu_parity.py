@@ -715,9 +715,12 @@ BLOCK_EPS = 1e-5
 # The GPU normalises in float32 and the oracle in float64, and each rounds x once
 # to bf16, so a few elements of x differ by one bf16 unit (test_rmsnorm_step bounds
 # how many). One such element moves a router logit by 2^-7 |x_j| |W_g[j, e]| at
-# most, so the routing of the block is compared with a near-tie margin of 1e-2 and
-# a gate-weight tolerance of 2e-3 instead of 1e-3 and 1e-5; the layer's output
-# tolerance is unchanged.
+# most, so against the oracle's own normalisation the routing of the block is
+# compared with a near-tie margin of 1e-2 and a gate-weight tolerance of 2e-3
+# instead of 1e-3 and 1e-5; the layer's output tolerance is unchanged. The routing
+# itself is also held to the layer's rule (1e-3, 1e-5) on the x the block routed:
+# moe_rmsnorm's output, bitwise the block's own (test_block_staged_equals_one_call),
+# routed by the oracle (_block_routing_strict).
 BLOCK_ROUTING = dict(tie_margin=1e-2, w_tol=2e-3)
 
 
@@ -758,6 +761,17 @@ def _run_block(moe, cfg, inp, blk, path="auto", out_dtype="f32"):
     return yh.astype(np.float64), parity.host_array(idx), parity.host_array(w), p, dev
 
 
+def _block_routing_strict(moe, oracle, inp, blk, cfg, p, idx_gpu, w_gpu):
+    """The block's routing against the oracle's router applied to the GPU's
+    normalised x, with the layer's near-tie margin and weight tolerance."""
+    x = moe.rmsnorm(p, parity.device_array(blk["h"], cfg.dtype),
+                    parity.device_array(blk["norm_w"], cfg.dtype), BLOCK_EPS)
+    torch.cuda.synchronize()
+    xg = parity.host_array(x)
+    l, idx, _, margin = oracle.route(xg, inp["w_g"], cfg.K, cfg.dtype)
+    parity.check_routing(idx_gpu, w_gpu, l, idx, margin, cfg.K, oracle)
+
+
 def _block_ref(oracle, inp, blk, cfg, tokens, idx_gpu, w_gpu):
     x, _ = oracle.rmsnorm(blk["h"], blk["norm_w"], BLOCK_EPS, cfg.dtype)
     toks, y_ref, diff, _ = _layer_ref(oracle, dict(inp, x=x), cfg, tokens, idx_gpu, w_gpu,
@@ -777,7 +791,8 @@ def test_block_forward(moe, oracle, name, cfg, path):
     oracle (the residual itself is added exactly in float32)."""
     inp = mi.make_inputs(cfg, seed=13)
     blk = mi.make_block(cfg, seed=13)
-    y, idx, w, _, _ = _run_block(moe, cfg, inp, blk, path)
+    y, idx, w, p, _ = _run_block(moe, cfg, inp, blk, path)
+    _block_routing_strict(moe, oracle, inp, blk, cfg, p, idx, w)
     toks, y_ref, h64, diff = _block_ref(oracle, inp, blk, cfg, np.arange(cfg.T), idx, w)
     parity.check_output(y[toks] - h64, y_ref, cfg.dtype, f"block {name} (MoE part)")
     # the output itself: residual + MoE part, float32 rounding of the sum only
@@ -827,8 +842,9 @@ def test_block_decode_workload(moe, oracle):
     cfg = mi.CONFIGS["decode_8x7b"]
     inp = mi.make_inputs(cfg, seed=0)
     blk = mi.make_block(cfg, seed=0)
-    y, idx, w, _, dev = _run_block(moe, cfg, inp, blk, "auto")
+    y, idx, w, p, dev = _run_block(moe, cfg, inp, blk, "auto")
     del dev
+    _block_routing_strict(moe, oracle, inp, blk, cfg, p, idx, w)
     toks, y_ref, h64, _ = _block_ref(oracle, inp, blk, cfg, np.arange(cfg.T), idx, w)
     parity.check_output(y[toks] - h64, y_ref, cfg.dtype, "block decode_8x7b (MoE part)")
 
