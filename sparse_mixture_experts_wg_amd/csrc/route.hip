@@ -210,31 +210,58 @@ __global__ __launch_bounds__(256) void route_wide_kernel(const uint16_t *__restr
   for (int i = 0; i < 64; ++i) v[i] = 0.f;
 
   // d / 4 is a multiple of 32, so a lane's 8 rows are all inside the quarter or
-  // all outside it
+  // all outside it. The full 512-row blocks run as a uniform loop that issues the
+  // next block's loads before the current block's arithmetic (two register
+  // buffers); the lanes of a last, partial block run after it under a lane mask.
+  // (With the lane test inside one loop the compiler ran the loop under an exec
+  // mask and waited for every load at the top of each block.) The sums are those of
+  // one block at a time, in the same order.
   const int rbeg = wave * (d >> 2), rend = rbeg + (d >> 2);
-  for (int j0 = rbeg; j0 < rend; j0 += 512) {
-    const int j = j0 + 8 * lane;
-    if (j >= rend) continue;
-    u32x4 xq[kWideTPB];
+  const int nfull = (rend - rbeg) >> 9;
+  u32x4 xq[2][kWideTPB], wq[2][8];
+  auto load_block = [&](int j, u32x4 *xb, u32x4 *wb) {
 #pragma unroll
     for (int t = 0; t < kWideTPB; ++t)  // a missing token re-reads the last one
-      xq[t] = *reinterpret_cast<const u32x4 *>(x + (tok0 + min(t, ntok - 1)) * d + j);
-    float wv[8][8];
+      xb[t] = *reinterpret_cast<const u32x4 *>(x + (tok0 + min(t, ntok - 1)) * d + j);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) load8<true>(wg, int64_t(j + r) * 8, wv[r]);
+    for (int r = 0; r < 8; ++r)
+      wb[r] = *reinterpret_cast<const u32x4 *>(wg + int64_t(j + r) * 8);
+  };
+  // row by row (each accumulator still adds rows r = 0..7 in order), so that only one
+  // row of weights is unpacked at a time
+  auto mac_block = [&](const u32x4 *xb, const u32x4 *wb) {
 #pragma unroll
-    for (int t = 0; t < kWideTPB; ++t) {
-      if (t >= ntok) continue;
-      float xv[8];
+    for (int r = 0; r < 8; ++r) {
+      float wv[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        xv[2 * i] = __uint_as_float(xq[t][i] << 16);
-        xv[2 * i + 1] = __uint_as_float(xq[t][i] & 0xFFFF0000u);
+        wv[2 * i] = __uint_as_float(wb[r][i] << 16);
+        wv[2 * i + 1] = __uint_as_float(wb[r][i] & 0xFFFF0000u);
       }
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
+      for (int t = 0; t < kWideTPB; ++t) {
+        if (t >= ntok) continue;
+        const uint32_t q = xb[t][r >> 1];
+        const float xv = __uint_as_float((r & 1) ? (q & 0xFFFF0000u) : (q << 16));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[t * 8 + e] = fmaf(xv[r], wv[r][e], v[t * 8 + e]);
+        for (int e = 0; e < 8; ++e) v[t * 8 + e] = fmaf(xv, wv[e], v[t * 8 + e]);
+      }
+    }
+  };
+  if (nfull > 0) load_block(rbeg + 8 * lane, xq[0], wq[0]);
+  int b = 0;
+  for (; b + 2 <= nfull; b += 2) {
+    load_block(rbeg + 512 * (b + 1) + 8 * lane, xq[1], wq[1]);  // (b + 1 < nfull)
+    mac_block(xq[0], wq[0]);
+    if (b + 2 < nfull) load_block(rbeg + 512 * (b + 2) + 8 * lane, xq[0], wq[0]);
+    mac_block(xq[1], wq[1]);
+  }
+  if (b < nfull) mac_block(xq[0], wq[0]);  // odd count: the last full block
+  {
+    const int j = rbeg + 512 * nfull + 8 * lane;  // partial block, if any
+    if (j < rend) {
+      load_block(j, xq[1], wq[1]);
+      mac_block(xq[1], wq[1]);
     }
   }
 
